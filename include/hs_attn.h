@@ -1,0 +1,233 @@
+/*
+ * hs_attn.h - C ABI of the MI355X (gfx950) query-guided block-sparse decode
+ * attention library `libhs_attn.so`.
+ *
+ * The library computes one decode step of hierarchical sparse attention in
+ * three stages, each an entry point below:
+ *
+ *   hs_build_summaries  per-block key summaries (mean-pooled keys, or the
+ *                       per-dimension key min/max "bounding box")
+ *   hs_select_blocks    score every block against the current query, keep a
+ *                       top-k (one or two levels) and always add the blocks of
+ *                       the local window
+ *   hs_sparse_decode    exact softmax attention over the selected blocks only,
+ *                       read in place from a paged KV cache
+ *
+ * Sources (web pages; cited by title and section):
+ *   [QSA]     "8x256K long-context sparse attention: porting HiSparse to QSA"
+ *             (xxmr.cn), sections 2.2 (three-level coarse/fine/window
+ *             selection), 2.3 (sparsify on block boundaries), 3.1 (C config
+ *             struct instead of a Python dict), 3.2 (selection on the GPU),
+ *             3.3 (attention loop over a compact index list), 5.1 (fp32
+ *             block scores).
+ *   [HiSp]    untitled HiSparse project write-up (trdm.cn), sections 3.1
+ *             (per-block table resident in HBM), 3.2 (64-token block slots),
+ *             3.3 (decode loop: force the window, then top-K), 4.1
+ *             (write/read-top-k wrapper).
+ *   [SGL]     "SGLang hierarchical sparse attention: analysis and practice"
+ *             (intelliparadigm.com), sections 2.2 (representation phase,
+ *             query-guided decode phase, logical->physical page table) and
+ *             3.1.2 (Quest: per-block key bounding boxes).
+ *   [SparDA]  SparDA article (2kiu.com), sections 2.3 (64-token blocks),
+ *             3.1 (mean-pooled block representatives), 3.3 (the kernel walks
+ *             only the selected pages), 3.4 (one selection shared by all
+ *             later layers and reused while decoding).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device; the
+ *     caller allocates and owns every buffer. The library allocates nothing,
+ *     keeps no state between calls and is reentrant (two calls may run at the
+ *     same time if they do not share output or workspace buffers).
+ *   - Struct arguments are read only during the call.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t, passed as
+ *     void*; NULL = the default stream). Outputs are valid once the stream
+ *     reaches that point.
+ *   - Every argument is validated on the host BEFORE any HIP call; an invalid
+ *     call returns an error code and enqueues nothing. A failed kernel launch
+ *     returns HS_ERR_HIP. No C++ exception crosses this boundary.
+ *   - Device-side values that the host cannot see (seq_lens, page-table
+ *     entries, block ids, counts) are range-checked in the kernels: a sequence
+ *     length is clamped to [0, max_seq_len]; a page-table entry outside
+ *     [0, num_phys_pages) makes its tokens count as absent; a block id outside
+ *     [0, ceil(T_b / block_size)) is skipped; a count is clamped to
+ *     [0, max_selected]. No such value can make a kernel read or write out
+ *     of bounds.
+ *   - Indexing: B = batch, Hkv = num_kv_heads, Hq = num_q_heads,
+ *     G = Hq / Hkv (query head h uses KV head h / G), d = head_dim,
+ *     P = page_size, S = block size of a summary level, T_b = seq_lens[b].
+ *     A "unit" is one (b, kv-head) pair; units are independent.
+ */
+#ifndef HS_ATTN_H
+#define HS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS_ATTN_VERSION 1
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = 1, /* null pointer, bad shape, inconsistent sizes     */
+  HS_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, group size, dtype */
+  HS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  HS_ERR_HIP = 4          /* a HIP launch failed                              */
+} hs_status;
+
+typedef enum { HS_F32 = 0, HS_BF16 = 1 } hs_dtype;
+
+typedef enum {
+  HS_SUMMARY_MEAN = 0,   /* mean-pooled keys [SparDA 3.1], [QSA 2.2]          */
+  HS_SUMMARY_MINMAX = 1  /* per-dimension key min and max [SGL 3.1.2]          */
+} hs_summary_kind;
+
+/* Paged KV cache of ONE layer ([SGL 2.2]: logical block -> physical page
+ * through a page table; [HiSp 3.2]: fixed-size token slots, contiguous inside
+ * a slot).
+ *   k_pool, v_pool : dtype[num_phys_pages][num_kv_heads][page_size][head_dim]
+ *                    token t of sequence b, KV head g lives in physical page
+ *                    page_table[b][t / P] at row (g, t % P).
+ *   page_table     : int32[batch][max_pages], logical page -> physical page.
+ *   seq_lens       : int32[batch], T_b, on the device.
+ *   max_seq_len    : host-side upper bound of every T_b (sizes the grids);
+ *                    must be <= max_pages * page_size.
+ * Supported: head_dim in {64, 128}; dtype HS_F32 or HS_BF16. */
+typedef struct {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t num_phys_pages;
+  int32_t max_seq_len;
+  int32_t dtype; /* hs_dtype */
+} hs_kv_cache;
+
+/* One level of block summaries, caller-allocated ([HiSp 3.1]: a small per-
+ * block table resident in HBM; [SGL 2.2]: key statistics kept on the GPU).
+ *   kind MEAN   : float32[batch][num_kv_heads][max_blocks][head_dim]
+ *                 row beta = mean of k_t over the valid tokens of block beta
+ *                 (fp32; [SparDA 3.1] mean pooling).
+ *   kind MINMAX : dtype[batch][num_kv_heads][max_blocks][2][head_dim]
+ *                 [..][0][i] = min_t k_t,i and [..][1][i] = max_t k_t,i over
+ *                 the valid tokens of block beta, in the KV dtype (exact).
+ *   block_size  : S (tokens per block), >= 1.
+ *   max_blocks  : rows per unit, >= ceil(max_seq_len / S).
+ * Rows at or beyond ceil(T_b / S) are left untouched by the build and never
+ * read by the selection. */
+typedef struct {
+  void* data;
+  int32_t kind;       /* hs_summary_kind */
+  int32_t block_size;
+  int32_t max_blocks;
+} hs_summaries;
+
+/* Selection parameters ([QSA 3.1]: a plain C struct instead of a per-request
+ * dictionary).
+ *   num_q_heads   : Hq; G = Hq / Hkv in {1, 2, 4, 8}. The block score of a
+ *                   unit is the SUM of the scores of its G query heads.
+ *   top_k         : k of the fine level ([QSA 2.2], [HiSp 3.3]); 0 = none.
+ *   window_tokens : W. Blocks holding any of tokens [T_b - W, T_b) are always
+ *                   selected ([QSA 2.2] window level, [HiSp 3.3] step one).
+ *   top_k_coarse  : 0 = single level. Otherwise the two-level scheme of
+ *                   [QSA 2.2]: top_k_coarse blocks of the `coarse` table, then
+ *                   top_k fine blocks among the fine blocks inside them.
+ *   max_selected  : row capacity of block_ids. Must be >= the largest possible
+ *                   count: min(max_blocks, min(top_k, max_blocks) +
+ *                   ceil(W / S) + 1). */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t top_k;
+  int32_t window_tokens;
+  int32_t top_k_coarse;
+  int32_t max_selected;
+} hs_select_params;
+
+/* Workspace sizes (bytes) for hs_select_blocks / hs_sparse_decode. Pure host
+ * functions: they validate like the matching entry point and write *bytes.
+ * `coarse` may be NULL for single-level selection. */
+hs_status hs_select_workspace_size(const hs_select_params* p,
+                                   const hs_kv_cache* kv,
+                                   const hs_summaries* fine,
+                                   const hs_summaries* coarse, size_t* bytes);
+hs_status hs_decode_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
+                                   int32_t block_size, int32_t max_selected,
+                                   size_t* bytes);
+
+/* Stage 1 - block summaries ([SGL 2.2] representation phase; [SGL 3.1.2]
+ * bounding boxes; [SparDA 3.1] / [QSA 2.2] mean pooling).
+ * Rebuilds, for every unit (b, g), rows beta in [block_begin, ceil(T_b / S))
+ * of `out` from the keys of k_pool. block_begin = 0 builds everything (after
+ * prefill); block_begin = ceil(T_b / S) - 1 refreshes only the last, growing
+ * block after a decode-time append. A partial last block is summarised over
+ * its valid tokens only. Only k_pool of `kv` is read (v_pool may be NULL). */
+hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin,
+                             const hs_summaries* out, void* stream);
+
+/* Stage 2 - query-guided block selection ([SGL 2.2] decode phase step a;
+ * [QSA 2.2] three-level scheme; [QSA 3.2] selection on the GPU; [QSA 5.1]
+ * fp32 scores).
+ *   q            : dtype[batch][Hq][head_dim], same dtype as the cache.
+ *   fine         : summaries of the fine level (block size S).
+ *   coarse       : NULL, or the coarse level (MEAN or MINMAX, block size C,
+ *                  C % S == 0) when p->top_k_coarse > 0.
+ * Score of block beta for unit (b, g), accumulated in fp32, unscaled:
+ *   MEAN   : s = sum_{j<G} q_j . mu_beta
+ *   MINMAX : s = sum_{j<G} sum_i max(q_j,i * m_beta,i, q_j,i * M_beta,i)
+ *            (the largest value q_j . k can take inside the box).
+ * Top-k orders candidates by score descending, then block index ascending,
+ * and keeps the first min(k, #candidates). Two-level: the candidates of the
+ * fine level are the fine blocks inside the top_k_coarse coarse blocks.
+ * Output per unit: the union of the top-k and the window blocks, sorted
+ * ascending, without duplicates:
+ *   block_ids    : int32[batch][Hkv][max_selected] (entries past the count
+ *                  are left untouched)
+ *   num_selected : int32[batch][Hkv]
+ * Only shapes and seq_lens of `kv` are used (pools may be NULL).
+ * workspace: device buffer of at least hs_select_workspace_size() bytes. */
+hs_status hs_select_blocks(const hs_select_params* p, const hs_kv_cache* kv,
+                           const void* q, const hs_summaries* fine,
+                           const hs_summaries* coarse, int32_t* block_ids,
+                           int32_t* num_selected, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Stage 3 - sparse paged decode attention ([QSA 3.3] loop over a compact
+ * index list of selected blocks; [SparDA 3.3] only the selected pages are
+ * read; [QSA 2.3] no gather into a compact copy).
+ * For query head h of unit (b, g = h / G), with A the tokens t < T_b of the
+ * blocks block_ids[b][g][0 .. num_selected[b][g]):
+ *   out[b][h] = sum_{t in A} exp(l_t - m) v_t / sum_{t in A} exp(l_t - m),
+ *   l_t = scale * q_h . k_t,  m = max_{t in A} l_t,
+ * fp32 softmax and accumulation. If A is empty, out[b][h] = 0.
+ *   q            : dtype[batch][Hq][head_dim]
+ *   scale        : logit scale; 0 means 1 / sqrt(head_dim)
+ *   block_size   : S of the ids (any S >= 1; need not equal page_size)
+ *   out          : float32[batch][Hq][head_dim]
+ * The same block_ids may be passed to the decode of every layer (shared
+ * selection, [SparDA 3.4]); they are only read.
+ * workspace: device buffer of at least hs_decode_workspace_size() bytes. */
+hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
+                           int32_t num_q_heads, float scale,
+                           int32_t block_size, const int32_t* block_ids,
+                           const int32_t* num_selected, int32_t max_selected,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* hs_status_string(hs_status s);
+
+/* HS_ATTN_VERSION of the built library. */
+int32_t hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS_ATTN_H */
