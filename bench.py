@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of query-guided block-sparse attention on one MI355X.
+
+Workload: the GQA 128K decode workload (batch 4, 32 query / 8 KV heads,
+head_dim 128, context 131072, bf16 KV with 16 needle blocks per KV head;
+Quest min/max summaries over 32-token blocks, top-128 blocks + 512-token
+window, selection shared by the 4 query heads of a KV group). Inputs are
+seeded synthetic data (synth/), resident in HBM before timing starts.
+
+One step = the whole decode-time path through the C ABI:
+  1. hs_build_summaries from the last block on (refresh of the growing block),
+  2. hs_select_blocks (score all 4096 blocks per unit, top-k, window union),
+  3. hs_sparse_decode (exact softmax attention over the selected blocks).
+
+The per-step working set (summaries + selected KV, ~143 MB) would fit in the
+256 MiB Infinity Cache, so the timed loop rotates over `--copies` identical
+copies of the inputs (at 8 copies every reuse is ~1 GB of traffic apart),
+which makes each step read from HBM. Steps are HIP-graph replays (one graph
+per copy) unless --no-graph.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg):
+    print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--event-steps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the path is measured on one GPU's share of the "
+              "work (--gpus %d was requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    from synth import device as sdev
+    from synth.workloads import CONFIGS
+
+    w = CONFIGS[args.config]
+    assert w.layers == 1 and w.top_k_coarse == 0, "bench workloads: single layer, single level"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    stream = torch.cuda.Stream()
+    esize = 2 if w.dtype == "bf16" else 4
+
+    # ------------------------------------------------------------ inputs
+    t = time.time()
+    log("generating %s inputs" % w.name)
+    kp0, vp0 = sdev.make_pools(w)
+    pt = sdev.page_table_tensor(w)
+    sl = sdev.seq_lens_tensor(w)
+    q0 = sdev.q_tensor(w)
+    torch.cuda.synchronize()
+    log("inputs on device in %.1f s (%.2f GB of K/V)" % (time.time() - t,
+                                                         2 * kp0.numel() * esize / 1e9))
+    cap = w.max_selected
+    copies = []
+    for c in range(args.copies):
+        kp = kp0 if c == 0 else kp0.clone()
+        vp = vp0 if c == 0 else vp0.clone()
+        kv = hs.KVCache(kp, vp, pt, sl, w.T)
+        fine = hs.Summaries.empty(kv, w.kind, w.S)
+        q = q0 if c == 0 else q0.clone()
+        ids = torch.zeros((w.batch, w.hkv, cap), dtype=torch.int32, device=dev)
+        cnt = torch.zeros((w.batch, w.hkv), dtype=torch.int32, device=dev)
+        out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device=dev)
+        ws_s = hs.workspace(hs.hs_select_workspace_size(kv, fine, w.hq, w.top_k, w.window, cap),
+                            dev)
+        ws_d = hs.workspace(hs.hs_decode_workspace_size(kv, w.hq, w.S, cap), dev)
+        copies.append(dict(kv=kv, fine=fine, q=q, ids=ids, cnt=cnt, out=out, ws_s=ws_s,
+                           ws_d=ws_d))
+    torch.cuda.synchronize()
+
+    # full summary build (prefill phase; reported separately, not part of a step)
+    build_ms = []
+    for c in copies:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        hs.hs_build_summaries(c["kv"], c["fine"], 0, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        build_ms.append(e0.elapsed_time(e1))
+    build_bytes = w.units * (w.T * w.d * esize + w.nb * 2 * w.d * esize)
+    build_avg = float(np.mean(build_ms[1:] if len(build_ms) > 1 else build_ms))
+    log("full summary build: %.3f ms, %.0f GB/s" % (build_avg, build_bytes / build_avg / 1e6))
+
+    last_block = (w.T - 1) // w.S
+    for c in copies:
+        c["calls"] = [
+            hs.prepare_build_summaries(c["kv"], c["fine"], last_block, stream),
+            hs.prepare_select_blocks(c["kv"], c["q"], c["fine"], w.top_k, w.window, c["ids"],
+                                     c["cnt"], c["ws_s"], stream),
+            hs.prepare_sparse_decode(c["kv"], c["q"], w.S, c["ids"], c["cnt"], c["out"],
+                                     c["ws_d"], stream),
+        ]
+
+    def step(c):
+        for call in c["calls"]:
+            call()
+
+    # ------------------------------------------------ per-call event timing
+    n_ev = args.event_steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    with torch.cuda.stream(stream):
+        for i in range(5):
+            step(copies[i % len(copies)])
+        for i in range(n_ev):
+            c = copies[i % len(copies)]
+            evs[i][0].record(stream)
+            for j, call in enumerate(c["calls"]):
+                call()
+                evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
+                         for i in range(n_ev)])
+    call_ms = per_call.mean(axis=0)
+    log("per-call mean ms: refresh %.4f select %.4f decode %.4f" % tuple(call_ms))
+
+    # ---------------------------------------------------------- graphs
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        for c in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(copies[i % len(copies)])
+
+    # ------------------------------------------------------- timed loop
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            run(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # warm (cache-resident) figure: one copy back to back, for context only
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run(0) if graphs is None else graphs[0].replay()
+        torch.cuda.synchronize()
+        tw0 = time.perf_counter()
+        for i in range(args.steps):
+            run(0) if graphs is None else graphs[0].replay()
+        torch.cuda.synchronize()
+        tw1 = time.perf_counter()
+    warm_ms = (tw1 - tw0) * 1e3 / args.steps
+
+    # ----------------------------------------------- algorithmic bytes
+    c0 = copies[0]
+    ids = c0["ids"].cpu().numpy()
+    cnt = c0["cnt"].cpu().numpy()
+    lens = w.seq_lens_array()
+    kv_tokens = 0
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            sel = ids[b, g, :cnt[b, g]].astype(np.int64)
+            kv_tokens += int(np.minimum(w.S, lens[b] - sel * w.S).sum())
+    row_bytes = (w.d * 4) if w.kind == "mean" else 2 * w.d * esize
+    q_bytes = w.batch * w.hq * w.d * esize
+    id_bytes = int(cnt.sum()) * 4 + w.units * 4
+    bytes_decode = kv_tokens * w.d * esize * 2 + q_bytes + id_bytes + w.batch * w.hq * w.d * 4
+    bytes_select = w.units * w.nb * row_bytes + q_bytes + id_bytes
+    bytes_refresh = w.units * (w.S * w.d * esize + row_bytes)
+    bytes_step = bytes_decode + bytes_select + bytes_refresh
+    log("bytes/step: select %.1f MB, decode %.1f MB (%d KV tokens), refresh %.2f MB" % (
+        bytes_select / 1e6, bytes_decode / 1e6, kv_tokens, bytes_refresh / 1e6))
+
+    dec_ms = float(call_ms[2])
+    sel_ms = float(call_ms[1])
+    dominant = "hs_sparse_decode" if bytes_decode >= bytes_select else "hs_select_blocks"
+    dom_bytes, dom_ms = ((bytes_decode, dec_ms) if dominant == "hs_sparse_decode"
+                         else (bytes_select, sel_ms))
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    qheads = w.batch * w.hq
+
+    # ----------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    result = {
+        "metric": "decode query-heads/sec at 128K ctx + effective HBM GB/s as % of MI355X peak",
+        "value": qheads / (ms_per_step * 1e-3),
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q with planted needle blocks)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.d, "context": w.T, "summary": w.kind, "block": w.S,
+                   "page": w.page_size, "top_k": w.top_k, "window": w.window,
+                   "graph": graphs is not None, "input_copies": len(copies)},
+        "effective_GBps": bytes_step / (ms_per_step * 1e-3) / 1e9,
+        "effective_frac_of_peak": bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "bytes_per_step": bytes_step,
+        "per_call_ms": {"hs_build_summaries(last block)": float(call_ms[0]),
+                        "hs_select_blocks": sel_ms, "hs_sparse_decode": dec_ms},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": dom_bytes, "avg_ms": dom_ms},
+        "select_roofline": {"achieved": bytes_select / (sel_ms * 1e-3) / 1e9,
+                            "bytes_per_launch": bytes_select, "avg_ms": sel_ms},
+        "summary_build": {"ms": build_avg, "GBps": build_bytes / build_avg / 1e6},
+        "warm_ms_per_step_single_copy": warm_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle, timed on this host: select (from precomputed oracle
+    summaries) + attention for a sample of units, repeated for ~`seconds`."""
+    import platform
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    units = [(0, 0), (1, 3), (2, 5), (3, 7)][:w.units]
+    log("cpu baseline: preparing %d units" % len(units))
+    prep = []
+    for b, g in units:
+        q = synth.widen(w.q(), w.dtype)[b, g * w.G:(g + 1) * w.G]
+        K = synth.widen(w.k_unit(0, b, g), w.dtype)
+        V = synth.widen(w.v_unit(0, b, g), w.dtype)
+        a, c = oracle.summarize(K, w.S, w.kind)
+        prep.append((q, K, V, (a, c, None, None)))
+    threads = min(len(units), len(os.sched_getaffinity(0)))
+
+    def one(i):
+        q, K, V, summ = prep[i]
+        sel = oracle.select_unit(q, K, w.T, w.kind, w.S, w.top_k, w.window, summaries=summ)
+        oracle.attend_unit(q, K, V, w.T, sel.ids, w.S)
+
+    reps = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(one, range(len(units))))
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    qh = reps * len(units) * w.G
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    log("cpu baseline: %d query-heads in %.1f s on %d threads" % (qh, dt, threads))
+    return {"value": qh / dt, "unit": "query-heads/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d units (b, kv-head) of the same workload, select from "
+                      "precomputed summaries + attention, repeated %d times (%.1f s)" % (
+                          len(units), w.units, reps, dt),
+            "cpu_model": model}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""Python binding of libhs_attn.so: query-guided block-sparse decode attention
+on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels. The
+functions keep the C names (hs_build_summaries, hs_select_blocks,
+hs_sparse_decode, ...) and take torch tensors, which only provide device
+memory; the current torch stream is used unless one is passed. There is no
+CPU fallback: if the library has not been built, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhs_attn.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP = range(5)
+HS_F32, HS_BF16 = 0, 1
+HS_SUMMARY_MEAN, HS_SUMMARY_MINMAX = 0, 1
+KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
+
+# Names declared in include/hs_attn.h; the CPU tests check that each is exported.
+EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
+           "hs_select_blocks", "hs_sparse_decode", "hs_status_string", "hs_version")
+
+
+class HsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s" % (fn, status_string(status)))
+
+
+class hs_kv_cache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_phys_pages", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class hs_summaries(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("kind", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class hs_select_params(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("window_tokens", ctypes.c_int32), ("top_k_coarse", ctypes.c_int32),
+                ("max_selected", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhs_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libhs_attn.so is not built; run "
+                              "`python -m hierarchical_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.hs_select_workspace_size.argtypes = [P(hs_select_params), P(hs_kv_cache),
+                                               P(hs_summaries), P(hs_summaries), P(sz)]
+        L.hs_decode_workspace_size.argtypes = [P(hs_kv_cache), i32, i32, i32, P(sz)]
+        L.hs_build_summaries.argtypes = [P(hs_kv_cache), i32, P(hs_summaries), vp]
+        L.hs_select_blocks.argtypes = [P(hs_select_params), P(hs_kv_cache), vp, P(hs_summaries),
+                                       P(hs_summaries), vp, vp, vp, sz, vp]
+        L.hs_sparse_decode.argtypes = [P(hs_kv_cache), vp, i32, ctypes.c_float, i32, vp, vp, i32,
+                                       vp, vp, sz, vp]
+        for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
+                     "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode"):
+            getattr(L, name).restype = ctypes.c_int
+        L.hs_status_string.argtypes = [ctypes.c_int]
+        L.hs_status_string.restype = ctypes.c_char_p
+        L.hs_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().hs_status_string(s).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != HS_OK:
+        raise HsError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libhs_attn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HS_F32
+    if t.dtype == torch.bfloat16:
+        return HS_BF16
+    raise ValueError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+@dataclass
+class KVCache:
+    """One layer's paged cache: pools [num_phys][Hkv][P][d], page_table
+    int32 [B][max_pages], seq_lens int32 [B] (all on the device)."""
+    k_pool: Optional[torch.Tensor]
+    v_pool: Optional[torch.Tensor]
+    page_table: torch.Tensor
+    seq_lens: torch.Tensor
+    max_seq_len: int
+    dtype: Optional[torch.dtype] = None
+    shape: Optional[tuple] = None  # (num_phys, Hkv, P, d) when pools are absent
+
+    def struct(self) -> hs_kv_cache:
+        ref = self.k_pool if self.k_pool is not None else self.v_pool
+        shape = tuple(ref.shape) if ref is not None else self.shape
+        dt = ref.dtype if ref is not None else self.dtype
+        if shape is None or dt is None:
+            raise ValueError("KVCache needs a pool or an explicit shape and dtype")
+        nphys, hkv, P, d = shape
+        for t in (self.page_table, self.seq_lens):
+            if t.dtype != torch.int32:
+                raise ValueError("page_table and seq_lens must be int32")
+        B, max_pages = self.page_table.shape
+        return hs_kv_cache(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.page_table),
+                           _ptr(self.seq_lens), B, hkv, d, P, max_pages, nphys,
+                           int(self.max_seq_len), HS_F32 if dt == torch.float32 else HS_BF16)
+
+
+@dataclass
+class Summaries:
+    """A summary table: mean -> float32 [B][Hkv][max_blocks][d];
+    minmax -> cache dtype [B][Hkv][max_blocks][2][d]."""
+    data: torch.Tensor
+    kind: str
+    block_size: int
+
+    @property
+    def max_blocks(self) -> int:
+        return self.data.shape[2]
+
+    def struct(self) -> hs_summaries:
+        return hs_summaries(_ptr(self.data), KIND[self.kind], self.block_size, self.max_blocks)
+
+    @staticmethod
+    def empty(kv: KVCache, kind: str, block_size: int, device=None) -> "Summaries":
+        s = kv.struct()
+        nb = -(-kv.max_seq_len // block_size)
+        dev = device or kv.page_table.device
+        dt = kv.k_pool.dtype if kv.k_pool is not None else kv.dtype
+        if kind == "mean":
+            t = torch.empty((s.batch, s.num_kv_heads, nb, s.head_dim), dtype=torch.float32,
+                            device=dev)
+        else:
+            t = torch.empty((s.batch, s.num_kv_heads, nb, 2, s.head_dim), dtype=dt, device=dev)
+        return Summaries(t, kind, block_size)
+
+
+# ------------------------------------------------------------ entry points
+def hs_select_workspace_size(kv: KVCache, fine: Summaries, num_q_heads: int, top_k: int,
+                             window: int, max_selected: int, coarse: Optional[Summaries] = None,
+                             top_k_coarse: int = 0) -> int:
+    p = hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected)
+    n = ctypes.c_size_t(0)
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    _check("hs_select_workspace_size",
+           lib().hs_select_workspace_size(ctypes.byref(p), ctypes.byref(ks), ctypes.byref(fs),
+                                          ctypes.byref(cs) if cs is not None else None,
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def hs_decode_workspace_size(kv: KVCache, num_q_heads: int, block_size: int,
+                             max_selected: int) -> int:
+    n = ctypes.c_size_t(0)
+    ks = kv.struct()
+    _check("hs_decode_workspace_size",
+           lib().hs_decode_workspace_size(ctypes.byref(ks), num_q_heads, block_size, max_selected,
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def hs_build_summaries(kv: KVCache, out: Summaries, block_begin: int = 0, stream=None) -> None:
+    ks, os_ = kv.struct(), out.struct()
+    _check("hs_build_summaries",
+           lib().hs_build_summaries(ctypes.byref(ks), block_begin, ctypes.byref(os_),
+                                    _stream(stream)))
+
+
+def hs_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                     block_ids: torch.Tensor, num_selected: torch.Tensor,
+                     workspace: torch.Tensor, coarse: Optional[Summaries] = None,
+                     top_k_coarse: int = 0, stream=None) -> None:
+    """q [B][Hq][d] in the cache dtype; block_ids int32 [B][Hkv][max_selected];
+    num_selected int32 [B][Hkv]; workspace a uint8 device tensor."""
+    if block_ids.dtype != torch.int32 or num_selected.dtype != torch.int32:
+        raise ValueError("block_ids and num_selected must be int32")
+    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    _check("hs_select_blocks",
+           lib().hs_select_blocks(ctypes.byref(p), ctypes.byref(ks), _ptr(q), ctypes.byref(fs),
+                                  ctypes.byref(cs) if cs is not None else None, _ptr(block_ids),
+                                  _ptr(num_selected), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+
+
+def hs_sparse_decode(kv: KVCache, q: torch.Tensor, block_size: int, block_ids: torch.Tensor,
+                     num_selected: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     scale: float = 0.0, stream=None) -> None:
+    """out float32 [B][Hq][d]; scale 0 means 1/sqrt(d)."""
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    ks = kv.struct()
+    _check("hs_sparse_decode",
+           lib().hs_sparse_decode(ctypes.byref(ks), _ptr(q), q.shape[1], float(scale), block_size,
+                                  _ptr(block_ids), _ptr(num_selected), block_ids.shape[-1],
+                                  _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+
+
+def hs_version() -> int:
+    return lib().hs_version()
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A uint8 device buffer of at least nbytes (256-byte aligned by torch)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class Prepared:
+    """An entry point with its arguments marshalled once; calling it issues
+    the C call on the given stream (for tight loops and graph capture). The
+    tensors it points to must stay alive and in place."""
+
+    def __init__(self, name: str, fn, args: tuple, keep: tuple):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != HS_OK:
+            raise HsError(self.name, st)
+
+
+def prepare_build_summaries(kv: KVCache, out: Summaries, block_begin: int, stream) -> Prepared:
+    ks, os_ = kv.struct(), out.struct()
+    return Prepared("hs_build_summaries", lib().hs_build_summaries,
+                    (ctypes.byref(ks), block_begin, ctypes.byref(os_), _stream(stream)),
+                    (ks, os_, kv, out))
+
+
+def prepare_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                          block_ids: torch.Tensor, num_selected: torch.Tensor,
+                          workspace: torch.Tensor, stream, coarse: Optional[Summaries] = None,
+                          top_k_coarse: int = 0) -> Prepared:
+    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    args = (ctypes.byref(p), ctypes.byref(ks), _ptr(q), ctypes.byref(fs),
+            ctypes.byref(cs) if cs is not None else None, _ptr(block_ids), _ptr(num_selected),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return Prepared("hs_select_blocks", lib().hs_select_blocks, args,
+                    (p, ks, fs, cs, kv, q, fine, coarse, block_ids, num_selected, workspace))
+
+
+def prepare_sparse_decode(kv: KVCache, q: torch.Tensor, block_size: int, block_ids: torch.Tensor,
+                          num_selected: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                          stream, scale: float = 0.0) -> Prepared:
+    ks = kv.struct()
+    args = (ctypes.byref(ks), _ptr(q), q.shape[1], ctypes.c_float(scale), block_size,
+            _ptr(block_ids), _ptr(num_selected), block_ids.shape[-1], _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    return Prepared("hs_sparse_decode", lib().hs_sparse_decode, args,
+                    (ks, kv, q, block_ids, num_selected, out, workspace))

@@ -1,0 +1,323 @@
+// capi.hip - the extern "C" boundary of libhs_attn.so: host-side argument
+// validation (before any HIP call), workspace layout and kernel dispatch.
+// The declarations and their contracts are in include/hs_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "hs_internal.h"
+
+namespace {
+
+using hs::KvView;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+hs_status check_kv(const hs_kv_cache* kv, bool need_k, bool need_v) {
+  if (!kv) return HS_ERR_INVALID_ARG;
+  if (kv->dtype != HS_F32 && kv->dtype != HS_BF16) return HS_ERR_UNSUPPORTED;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return HS_ERR_UNSUPPORTED;
+  if (!kv->page_table || !kv->seq_lens) return HS_ERR_INVALID_ARG;
+  if (kv->batch < 1 || kv->num_kv_heads < 1) return HS_ERR_INVALID_ARG;
+  if ((int64_t)kv->batch * kv->num_kv_heads > 65535) return HS_ERR_UNSUPPORTED;
+  if (kv->page_size < 1 || kv->max_pages < 1 || kv->num_phys_pages < 1) return HS_ERR_INVALID_ARG;
+  if (kv->max_seq_len < 0 || (int64_t)kv->max_seq_len > (int64_t)kv->max_pages * kv->page_size)
+    return HS_ERR_INVALID_ARG;
+  if (need_k && (!kv->k_pool || !aligned16(kv->k_pool))) return HS_ERR_INVALID_ARG;
+  if (need_v && (!kv->v_pool || !aligned16(kv->v_pool))) return HS_ERR_INVALID_ARG;
+  return HS_OK;
+}
+
+KvView view_of(const hs_kv_cache* kv) {
+  KvView v;
+  v.k_pool = static_cast<const uint8_t*>(kv->k_pool);
+  v.v_pool = static_cast<const uint8_t*>(kv->v_pool);
+  v.page_table = kv->page_table;
+  v.seq_lens = kv->seq_lens;
+  v.batch = kv->batch;
+  v.num_kv_heads = kv->num_kv_heads;
+  v.head_dim = kv->head_dim;
+  v.page_size = kv->page_size;
+  v.max_pages = kv->max_pages;
+  v.num_phys_pages = kv->num_phys_pages;
+  v.max_seq_len = kv->max_seq_len;
+  v.elem_bytes = kv->dtype == HS_BF16 ? 2 : 4;
+  return v;
+}
+
+// blocks a level can have per unit
+int64_t blocks_needed(const hs_kv_cache* kv, int32_t block_size) {
+  return ceil_div(kv->max_seq_len, block_size);
+}
+
+hs_status check_summ(const hs_summaries* s, const hs_kv_cache* kv) {
+  if (!s || !s->data || !aligned16(s->data)) return HS_ERR_INVALID_ARG;
+  if (s->kind != HS_SUMMARY_MEAN && s->kind != HS_SUMMARY_MINMAX) return HS_ERR_INVALID_ARG;
+  if (s->block_size < 1 || s->max_blocks < 1) return HS_ERR_INVALID_ARG;
+  if (s->max_blocks > hs::kMaxBlocks) return HS_ERR_UNSUPPORTED;
+  if ((int64_t)s->max_blocks < blocks_needed(kv, s->block_size)) return HS_ERR_INVALID_ARG;
+  return HS_OK;
+}
+
+int group_size(const hs_kv_cache* kv, int32_t num_q_heads, hs_status* st) {
+  *st = HS_OK;
+  if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads != 0) {
+    *st = HS_ERR_INVALID_ARG;
+    return 0;
+  }
+  const int G = num_q_heads / kv->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) *st = HS_ERR_UNSUPPORTED;
+  return G;
+}
+
+// Workspace of hs_select_blocks (byte offsets).
+struct SelectLayout {
+  bool two_level;
+  int64_t units, nb_fine, nc, kc_cap, ratio, fine_slots;
+  size_t off_coarse_scores, off_gamma, off_gamma_cnt, off_fine_scores, total;
+};
+
+hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
+                       const hs_summaries* fine, const hs_summaries* coarse, SelectLayout* L) {
+  if (!p) return HS_ERR_INVALID_ARG;
+  hs_status st = check_kv(kv, false, false);
+  if (st != HS_OK) return st;
+  group_size(kv, p->num_q_heads, &st);
+  if (st != HS_OK) return st;
+  st = check_summ(fine, kv);
+  if (st != HS_OK) return st;
+  if (p->top_k < 0 || p->window_tokens < 0 || p->top_k_coarse < 0) return HS_ERR_INVALID_ARG;
+  const bool two = p->top_k_coarse > 0;
+  if (two) {
+    st = check_summ(coarse, kv);
+    if (st != HS_OK) return st;
+    if (coarse->block_size % fine->block_size != 0) return HS_ERR_INVALID_ARG;
+  }
+  const int64_t S = fine->block_size;
+  const int64_t nb = blocks_needed(kv, fine->block_size);
+  const int64_t need = std::min<int64_t>(
+      fine->max_blocks,
+      std::min<int64_t>(p->top_k, fine->max_blocks) + ceil_div(p->window_tokens, S) + 1);
+  if (p->max_selected < need || p->max_selected < 1) return HS_ERR_INVALID_ARG;
+
+  L->two_level = two;
+  L->units = (int64_t)kv->batch * kv->num_kv_heads;
+  L->nb_fine = nb > 0 ? nb : 1;
+  size_t off = 0;
+  if (two) {
+    L->nc = std::max<int64_t>(1, blocks_needed(kv, coarse->block_size));
+    L->kc_cap = std::min<int64_t>(p->top_k_coarse, L->nc);
+    L->ratio = coarse->block_size / fine->block_size;
+    L->fine_slots = std::max<int64_t>(1, L->kc_cap * L->ratio);
+    L->off_coarse_scores = off;
+    off = align_up(off + sizeof(float) * L->units * L->nc);
+    L->off_gamma = off;
+    off = align_up(off + sizeof(int32_t) * L->units * L->kc_cap);
+    L->off_gamma_cnt = off;
+    off = align_up(off + sizeof(int32_t) * L->units);
+  } else {
+    L->nc = L->kc_cap = 0;
+    L->ratio = 1;
+    L->fine_slots = L->nb_fine;
+    L->off_coarse_scores = L->off_gamma = L->off_gamma_cnt = 0;
+  }
+  L->off_fine_scores = off;
+  off = align_up(off + sizeof(float) * L->units * L->fine_slots);
+  L->total = off;
+  return HS_OK;
+}
+
+struct DecodeLayout {
+  int64_t units, bps, max_splits, G;
+  size_t off_o, off_ml, total;
+};
+
+hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block_size,
+                       int32_t max_selected, DecodeLayout* L) {
+  hs_status st = check_kv(kv, true, true);
+  if (st != HS_OK) return st;
+  const int G = group_size(kv, num_q_heads, &st);
+  if (st != HS_OK) return st;
+  if (block_size < 1 || max_selected < 1) return HS_ERR_INVALID_ARG;
+  L->units = (int64_t)kv->batch * kv->num_kv_heads;
+  L->G = G;
+  L->bps = hs::decode_blocks_per_split(block_size);
+  L->max_splits = ceil_div(max_selected, L->bps);
+  if (L->max_splits > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
+  L->off_o = 0;
+  L->off_ml = align_up(sizeof(float) * L->units * L->max_splits * G * kv->head_dim);
+  L->total = align_up(L->off_ml + sizeof(float) * L->units * L->max_splits * G * 2);
+  return HS_OK;
+}
+
+hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hs_status_string(hs_status s) {
+  switch (s) {
+    case HS_OK: return "HS_OK";
+    case HS_ERR_INVALID_ARG: return "HS_ERR_INVALID_ARG";
+    case HS_ERR_UNSUPPORTED: return "HS_ERR_UNSUPPORTED";
+    case HS_ERR_WORKSPACE: return "HS_ERR_WORKSPACE";
+    case HS_ERR_HIP: return "HS_ERR_HIP";
+  }
+  return "HS_UNKNOWN_STATUS";
+}
+
+int32_t hs_version(void) { return HS_ATTN_VERSION; }
+
+hs_status hs_select_workspace_size(const hs_select_params* p, const hs_kv_cache* kv,
+                                   const hs_summaries* fine, const hs_summaries* coarse,
+                                   size_t* bytes) {
+  if (!bytes) return HS_ERR_INVALID_ARG;
+  SelectLayout L;
+  const hs_status st = check_select(p, kv, fine, coarse, &L);
+  if (st == HS_OK) *bytes = L.total;
+  return st;
+}
+
+hs_status hs_decode_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
+                                   int32_t block_size, int32_t max_selected, size_t* bytes) {
+  if (!bytes) return HS_ERR_INVALID_ARG;
+  DecodeLayout L;
+  const hs_status st = check_decode(kv, num_q_heads, block_size, max_selected, &L);
+  if (st == HS_OK) *bytes = L.total;
+  return st;
+}
+
+hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin, const hs_summaries* out,
+                             void* stream) {
+  hs_status st = check_kv(kv, true, false);
+  if (st != HS_OK) return st;
+  st = check_summ(out, kv);
+  if (st != HS_OK) return st;
+  if (block_begin < 0) return HS_ERR_INVALID_ARG;
+  hs::SummParams p;
+  p.kv = view_of(kv);
+  p.out = out->data;
+  p.kind = out->kind;
+  p.block_size = out->block_size;
+  p.max_blocks = out->max_blocks;
+  p.block_begin = block_begin;
+  return from_hip(hs::launch_build_summaries(p, static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                           const hs_summaries* fine, const hs_summaries* coarse,
+                           int32_t* block_ids, int32_t* num_selected, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  SelectLayout L;
+  hs_status st = check_select(prm, kv, fine, coarse, &L);
+  if (st != HS_OK) return st;
+  if (!q || !aligned16(q) || !block_ids || !num_selected) return HS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int G = prm->num_q_heads / kv->num_kv_heads;
+  const KvView view = view_of(kv);
+
+  hs::ScoreParams sp;
+  sp.kv = view;
+  sp.q = q;
+  sp.G = G;
+  hs::TopkParams tp;
+  tp.kv = view;
+  hipError_t e;
+  int32_t* gamma = nullptr;
+  int32_t* gamma_cnt = nullptr;
+  if (L.two_level) {
+    float* cs = reinterpret_cast<float*>(ws + L.off_coarse_scores);
+    gamma = reinterpret_cast<int32_t*>(ws + L.off_gamma);
+    gamma_cnt = reinterpret_cast<int32_t*>(ws + L.off_gamma_cnt);
+    sp.summ = coarse->data;
+    sp.kind = coarse->kind;
+    sp.block_size = coarse->block_size;
+    sp.max_blocks = coarse->max_blocks;
+    sp.gamma = nullptr;
+    sp.gamma_cnt = nullptr;
+    sp.gamma_cap = 0;
+    sp.ratio = 1;
+    sp.n_slots_max = (int32_t)L.nc;
+    sp.scores = cs;
+    if ((e = hs::launch_scores(sp, s)) != hipSuccess) return from_hip(e);
+    tp.scores = cs;
+    tp.n_slots_max = (int32_t)L.nc;
+    tp.block_size = coarse->block_size;
+    tp.top_k = prm->top_k_coarse;
+    tp.window = 0;
+    tp.gamma = nullptr;
+    tp.gamma_cnt = nullptr;
+    tp.gamma_cap = 0;
+    tp.ratio = 1;
+    tp.out_ids = gamma;
+    tp.out_cnt = gamma_cnt;
+    tp.out_cap = (int32_t)L.kc_cap;
+    tp.out_blocks_max = (int32_t)L.nc;
+    if ((e = hs::launch_topk(tp, s)) != hipSuccess) return from_hip(e);
+  }
+  float* fs = reinterpret_cast<float*>(ws + L.off_fine_scores);
+  sp.summ = fine->data;
+  sp.kind = fine->kind;
+  sp.block_size = fine->block_size;
+  sp.max_blocks = fine->max_blocks;
+  sp.gamma = gamma;
+  sp.gamma_cnt = gamma_cnt;
+  sp.gamma_cap = (int32_t)L.kc_cap;
+  sp.ratio = (int32_t)L.ratio;
+  sp.n_slots_max = (int32_t)L.fine_slots;
+  sp.scores = fs;
+  if ((e = hs::launch_scores(sp, s)) != hipSuccess) return from_hip(e);
+  tp.scores = fs;
+  tp.n_slots_max = (int32_t)L.fine_slots;
+  tp.block_size = fine->block_size;
+  tp.top_k = prm->top_k;
+  tp.window = prm->window_tokens;
+  tp.gamma = gamma;
+  tp.gamma_cnt = gamma_cnt;
+  tp.gamma_cap = (int32_t)L.kc_cap;
+  tp.ratio = (int32_t)L.ratio;
+  tp.out_ids = block_ids;
+  tp.out_cnt = num_selected;
+  tp.out_cap = prm->max_selected;
+  tp.out_blocks_max = (int32_t)L.nb_fine;
+  return from_hip(hs::launch_topk(tp, s));
+}
+
+hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q, int32_t num_q_heads, float scale,
+                           int32_t block_size, const int32_t* block_ids,
+                           const int32_t* num_selected, int32_t max_selected, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeLayout L;
+  hs_status st = check_decode(kv, num_q_heads, block_size, max_selected, &L);
+  if (st != HS_OK) return st;
+  if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
+  if (scale == 0.f) scale = 1.0f / sqrtf((float)kv->head_dim);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hs::DecodeParams p;
+  p.kv = view_of(kv);
+  p.q = q;
+  p.G = (int32_t)L.G;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.block_size = block_size;
+  p.ids = block_ids;
+  p.counts = num_selected;
+  p.max_selected = max_selected;
+  p.blocks_per_split = (int32_t)L.bps;
+  p.max_splits = (int32_t)L.max_splits;
+  p.part_o = reinterpret_cast<float*>(ws + L.off_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
+  p.out = out;
+  return from_hip(hs::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

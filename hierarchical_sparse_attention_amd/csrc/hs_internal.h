@@ -1,0 +1,179 @@
+// hs_internal.h - device helpers and kernel-launch declarations shared by the
+// HIP sources of libhs_attn.so (gfx950 / CDNA4, wave64). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hs_attn.h"
+
+namespace hs {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 16 bytes of storage -> EPL floats (EPL = 4 for float32, 8 for bfloat16).
+template <typename TE>
+struct Vec16;
+
+template <>
+struct Vec16<float> {
+  static constexpr int EPL = 4;
+  __device__ __forceinline__ static void unpack(const uint4& r, float* f) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  }
+};
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int EPL = 8;
+  __device__ __forceinline__ static void unpack(const uint4& r, float* f) {
+    f[0] = bf16_lo(r.x);
+    f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y);
+    f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z);
+    f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w);
+    f[7] = bf16_hi(r.w);
+  }
+};
+
+// Monotone map of a float32 to uint32: a < b (as floats, -0 == +0) iff
+// key(a) < key(b). Negative values have all bits flipped, non-negative ones
+// only the sign bit; -0 is mapped like +0. Finite inputs give keys >= 0x00800000.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------ cross-lane reduction
+// Sum over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32, 64}); every
+// lane of a group ends with the group's sum. Within a 16-lane DPP row the
+// butterfly uses quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and
+// row_mirror (after the two quad steps every lane of a quad holds the quad's
+// sum, so the mirrors pair whole quads, then whole half-rows); wider groups
+// exchange with the lanes 16 and 32 apart.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// ------------------------------------------------------------- cache access
+struct KvView {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int32_t batch, num_kv_heads, head_dim, page_size, max_pages, num_phys_pages, max_seq_len;
+  int32_t elem_bytes;
+};
+
+__device__ __forceinline__ int clamp_len(const KvView& kv, int b) {
+  int t = kv.seq_lens[b];
+  t = t < 0 ? 0 : t;
+  return t > kv.max_seq_len ? kv.max_seq_len : t;
+}
+
+// Byte offset of row (b, g, t) in a pool, or -1 if its page id is invalid.
+__device__ __forceinline__ int64_t row_offset(const KvView& kv, int b, int g, int t) {
+  int page = kv.page_table[(int64_t)b * kv.max_pages + t / kv.page_size];
+  if ((unsigned)page >= (unsigned)kv.num_phys_pages) return -1;
+  return (((int64_t)page * kv.num_kv_heads + g) * kv.page_size + t % kv.page_size) *
+         (int64_t)kv.head_dim * kv.elem_bytes;
+}
+
+// -------------------------------------------------------- launch interfaces
+struct SummParams {
+  KvView kv;
+  void* out;
+  int32_t kind, block_size, max_blocks, block_begin;
+};
+hipError_t launch_build_summaries(const SummParams& p, hipStream_t s);
+
+struct ScoreParams {
+  KvView kv;                 // shapes + seq_lens
+  const void* q;             // [B][Hq][d]
+  const void* summ;          // summary table
+  int32_t kind, block_size, max_blocks;
+  int32_t G;
+  // candidate slots: single level -> slot c is block c (n_slots = ceil(T_b/S));
+  // two-level fine -> slot c is block gamma[c / R] * R + c % R.
+  const int32_t* gamma;      // [units][gamma_cap] ascending coarse ids, or null
+  const int32_t* gamma_cnt;  // [units]
+  int32_t gamma_cap, ratio;  // R = C / S
+  int32_t n_slots_max;       // scores row length
+  float* scores;             // [units][n_slots_max]
+};
+hipError_t launch_scores(const ScoreParams& p, hipStream_t s);
+
+struct TopkParams {
+  KvView kv;
+  const float* scores;       // [units][n_slots_max]
+  int32_t n_slots_max;
+  int32_t block_size;        // S of the output ids (fine) or C (coarse)
+  int32_t top_k;
+  int32_t window;            // tokens (0 = none)
+  const int32_t* gamma;      // two-level fine: ascending coarse ids, else null
+  const int32_t* gamma_cnt;
+  int32_t gamma_cap, ratio;
+  int32_t* out_ids;          // [units][out_cap]
+  int32_t* out_cnt;          // [units]
+  int32_t out_cap;
+  int32_t out_blocks_max;    // blocks of the output level per unit (bitmap bits)
+};
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+
+struct DecodeParams {
+  KvView kv;
+  const void* q;
+  int32_t G;
+  float scale_log2;          // scale * log2(e)
+  int32_t block_size;
+  const int32_t* ids;
+  const int32_t* counts;
+  int32_t max_selected;
+  int32_t blocks_per_split, max_splits;
+  float* part_o;             // [units][max_splits][G][d]
+  float* part_ml;            // [units][max_splits][G][2]
+  float* out;                // [B][Hq][d]
+};
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+int decode_blocks_per_split(int block_size);
+
+constexpr int kMaxBlocks = 1 << 20;  // blocks per unit a selection level may have
+
+}  // namespace hs

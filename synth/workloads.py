@@ -151,30 +151,41 @@ class Workload:
     def _unit_start(self, b: int, g: int) -> int:
         return (b * self.hkv + g) * self.T * self.d
 
+    def plant_needles(self, k: np.ndarray, b: int, g: int) -> None:
+        """Overwrite the needle blocks of unit (b, g) in its key rows k [T][d]."""
+        blocks = self.needle_blocks(b, g)
+        if not len(blocks):
+            return
+        qd = self.q_dir(b, g)
+        unit = b * self.hkv + g
+        for ni, beta in enumerate(blocks):
+            t0 = int(beta) * self.S
+            t1 = min(t0 + self.S, self.T)
+            cnt = (t1 - t0) * self.d
+            z = normal(self.seed, STREAM_NEEDLE_NOISE,
+                       ((unit * self.needles + ni) * self.S) * self.d, cnt)
+            rows = 3.0 * qd[None, :] + z.reshape(t1 - t0, self.d)
+            k[t0:t1] = round_to(rows, self.dtype)
+
+    def kv_rows(self, which: str, layer: int, b: int, g0: int = 0, g1: Optional[int] = None):
+        """Rows of units (b, g0) .. (b, g1 - 1) as [g1 - g0][T][d] in the cache
+        dtype ('k' has the needles planted on layer 0)."""
+        g1 = self.hkv if g1 is None else g1
+        stream = (STREAM_K if which == "k" else STREAM_V) + LAYER_STRIDE * layer
+        n = (g1 - g0) * self.T * self.d
+        x = normal(self.seed, stream, self._unit_start(b, g0), n, self.dtype)
+        x = x.reshape(g1 - g0, self.T, self.d)
+        if which == "k" and layer == 0 and self.needles > 0:
+            for g in range(g0, g1):
+                self.plant_needles(x[g - g0], b, g)
+        return x
+
     def k_unit(self, layer: int, b: int, g: int) -> np.ndarray:
         """Keys of unit (b, g): [T][d] in the cache dtype, needles planted."""
-        n = self.T * self.d
-        k = normal(self.seed, STREAM_K + LAYER_STRIDE * layer, self._unit_start(b, g), n,
-                   self.dtype).reshape(self.T, self.d)
-        if layer == 0 and self.needles > 0:
-            blocks = self.needle_blocks(b, g)
-            if len(blocks):
-                qd = self.q_dir(b, g)
-                unit = b * self.hkv + g
-                for ni, beta in enumerate(blocks):
-                    t0 = int(beta) * self.S
-                    t1 = min(t0 + self.S, self.T)
-                    cnt = (t1 - t0) * self.d
-                    z = normal(self.seed, STREAM_NEEDLE_NOISE,
-                               ((unit * self.needles + ni) * self.S) * self.d, cnt)
-                    rows = 3.0 * qd[None, :] + z.reshape(t1 - t0, self.d)
-                    k[t0:t1] = round_to(rows, self.dtype)
-        return k
+        return self.kv_rows("k", layer, b, g, g + 1)[0]
 
     def v_unit(self, layer: int, b: int, g: int) -> np.ndarray:
-        n = self.T * self.d
-        return normal(self.seed, STREAM_V + LAYER_STRIDE * layer, self._unit_start(b, g), n,
-                      self.dtype).reshape(self.T, self.d)
+        return self.kv_rows("v", layer, b, g, g + 1)[0]
 
     # -- whole pools (small workloads only) -------------------------------
     def pools(self, layer: int = 0):

@@ -1,0 +1,159 @@
+"""Helpers for the GPU parity tests: put a workload on the device, run the
+library's three entry points, run the oracle on chosen units and compare.
+
+Comparison rules (stated by the target of the build, with the readings of
+the open points):
+  * block ids: bit-exact, except blocks whose oracle score lies within
+    1e-6 * max(|s_k|, sum_j sum_i |q_j,i x_beta,i|) of the oracle's k-th kept
+    score s_k (a near tie that fp32 accumulation order may resolve either
+    way); window blocks must always be present;
+  * outputs: per output row (b, h), ||o_gpu - o_ref||_inf / ||o_ref||_inf
+    <= 2e-3 for bf16 caches and <= 1e-5 for fp32 caches; the GPU path
+    accumulates in fp32 on exactly the stored inputs, so it is also held to
+    KERNEL_RTOL = 2e-5 (fp32 rounding of a <=10^4-term softmax), which catches
+    a dropped or doubled token that the looser bound could let through.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import hierarchical_sparse_attention_amd as hs
+import oracle
+import synth
+from synth import device as sdev
+from synth.workloads import Workload
+
+NORTH_STAR_RTOL = {"bf16": 2e-3, "f32": 1e-5}
+KERNEL_RTOL = 2e-5
+TIE_RTOL = 1e-6
+
+
+def log(msg: str) -> None:
+    print("[%s] %s" % (time.strftime("%H:%M:%S"), msg), flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Problem:
+    w: Workload
+    layers: int = 1
+    kvs: List[hs.KVCache] = field(default_factory=list)
+    page_table: Optional[torch.Tensor] = None
+    seq_lens: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def make(w: Workload, layers: int = 1) -> "Problem":
+        p = Problem(w=w, layers=layers)
+        p.page_table = sdev.page_table_tensor(w)
+        p.seq_lens = sdev.seq_lens_tensor(w)
+        for layer in range(layers):
+            kp, vp = sdev.make_pools(w, layer)
+            p.kvs.append(hs.KVCache(kp, vp, p.page_table, p.seq_lens, w.T))
+        torch.cuda.synchronize()
+        return p
+
+    def q(self, layer=0, step=0) -> torch.Tensor:
+        return sdev.q_tensor(self.w, layer, step)
+
+    def summaries(self, layer=0) -> Dict[str, hs.Summaries]:
+        w, kv = self.w, self.kvs[layer]
+        fine = hs.Summaries.empty(kv, w.kind, w.S)
+        hs.hs_build_summaries(kv, fine)
+        out = {"fine": fine}
+        if w.top_k_coarse:
+            coarse = hs.Summaries.empty(kv, "mean", w.coarse_S)
+            hs.hs_build_summaries(kv, coarse)
+            out["coarse"] = coarse
+        return out
+
+    def select(self, q: torch.Tensor, summ: Dict[str, hs.Summaries], top_k=None, window=None,
+               max_selected=None):
+        w, kv = self.w, self.kvs[0]
+        k = w.top_k if top_k is None else top_k
+        W = w.window if window is None else window
+        cap = max_selected or min(w.nb, min(k, w.nb) + -(-W // w.S) + 1)
+        ids = torch.full((w.batch, w.hkv, cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+        coarse = summ.get("coarse")
+        n = hs.hs_select_workspace_size(kv, summ["fine"], w.hq, k, W, cap, coarse, w.top_k_coarse)
+        ws = hs.workspace(n, "cuda")
+        hs.hs_select_blocks(kv, q, summ["fine"], k, W, ids, cnt, ws, coarse, w.top_k_coarse)
+        return ids, cnt
+
+    def decode(self, q: torch.Tensor, ids: torch.Tensor, cnt: torch.Tensor, layer=0,
+               block_size=None):
+        w, kv = self.w, self.kvs[layer]
+        S = w.S if block_size is None else block_size
+        n = hs.hs_decode_workspace_size(kv, w.hq, S, ids.shape[-1])
+        ws = hs.workspace(n, "cuda")
+        out = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+        hs.hs_sparse_decode(kv, q, S, ids, cnt, out, ws)
+        return out
+
+
+def unit_inputs(w: Workload, layer: int, b: int, g: int, step: int = 0):
+    """Oracle-side inputs of one unit: q [G][d], K and V rows [T][d] (float64)."""
+    q = synth.widen(w.q(layer, step), w.dtype)[b, g * w.G:(g + 1) * w.G]
+    K = synth.widen(w.k_unit(layer, b, g), w.dtype)
+    V = synth.widen(w.v_unit(layer, b, g), w.dtype)
+    return q, K, V
+
+
+def oracle_select(w: Workload, q, K, T, top_k=None, window=None):
+    k = w.top_k if top_k is None else top_k
+    W = w.window if window is None else window
+    return oracle.select_unit(q, K, T, w.kind, w.S, k, W, coarse_S=w.coarse_S,
+                              top_k_coarse=w.top_k_coarse)
+
+
+def magnitudes(w: Workload, q, K, T) -> np.ndarray:
+    """sum_j sum_i |q_j,i| * |x_beta,i| for every fine block (the scale of
+    the terms that make up a block score)."""
+    a, b = oracle.summarize(K[:T], w.S, w.kind)
+    x = np.abs(a) if b is None else np.maximum(np.abs(a), np.abs(b))
+    return x @ np.abs(q).sum(axis=0)
+
+
+def check_ids(w: Workload, gpu_ids: np.ndarray, sel: oracle.UnitSelection, mags: np.ndarray,
+              T: int, window=None, what="") -> int:
+    """Assert the near-tie rule; returns the number of tolerated differences."""
+    W = w.window if window is None else window
+    g = gpu_ids.tolist()
+    assert g == sorted(set(g)), "%s: ids not strictly ascending: %s" % (what, g[:20])
+    diff = set(g) ^ set(sel.ids.tolist())
+    if not diff:
+        return 0
+    win = set(oracle.window_blocks(T, w.S, W).tolist())
+    sk = sel.kth_score
+    for beta in diff:
+        assert beta not in win, "%s: window block %d missing" % (what, beta)
+        s = sel.fine_scores[beta] if 0 <= beta < len(sel.fine_scores) else float("nan")
+        assert not math.isnan(s), "%s: block %d was not a candidate" % (what, beta)
+        tol = TIE_RTOL * max(abs(sk), mags[beta])
+        assert abs(s - sk) <= tol, ("%s: block %d differs, score %.9g vs k-th %.9g (tol %.3g)"
+                                    % (what, beta, s, sk, tol))
+    return len(diff)
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per output row ||got - ref||_inf / ||ref||_inf (0 where both are zero)."""
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def check_rows(w: Workload, got: np.ndarray, ref: np.ndarray, what="") -> float:
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    err = float(row_rel_err(got, ref).max()) if got.size else 0.0
+    tol = NORTH_STAR_RTOL[w.dtype]
+    assert err <= tol, "%s: max row rel err %.3g > %.3g" % (what, err, tol)
+    assert err <= KERNEL_RTOL, "%s: max row rel err %.3g > kernel bound %.3g" % (
+        what, err, KERNEL_RTOL)
+    return err

@@ -1,0 +1,153 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every
+symbol include/hs_attn.h declares, and rejects invalid arguments on the host
+before any HIP call. No call here reaches a kernel launch: every call either
+is a pure host function or fails validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_sparse_attention_amd as hs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs_attn.h")
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = hs.lib()
+    names = declared_functions()
+    assert set(names) == set(hs.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert hs.hs_version() == 1
+
+
+def test_status_strings():
+    assert hs.status_string(hs.HS_OK) == "HS_OK"
+    assert hs.status_string(hs.HS_ERR_WORKSPACE) == "HS_ERR_WORKSPACE"
+    assert hs.status_string(99) == "HS_UNKNOWN_STATUS"
+
+
+def kv_struct(**over):
+    f = dict(k_pool=FAKE, v_pool=FAKE + 4096, page_table=FAKE + 8192, seq_lens=FAKE + 12288,
+             batch=4, num_kv_heads=8, head_dim=128, page_size=32, max_pages=4096,
+             num_phys_pages=4 * 4096, max_seq_len=131072, dtype=hs.HS_BF16)
+    f.update(over)
+    return hs.hs_kv_cache(**f)
+
+
+def summ(kind=hs.HS_SUMMARY_MINMAX, S=32, max_blocks=4096, data=FAKE + 65536):
+    return hs.hs_summaries(data, kind, S, max_blocks)
+
+
+def sel_size(p, kv, fine, coarse=None):
+    n = ctypes.c_size_t(0)
+    st = hs.lib().hs_select_workspace_size(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(fine),
+                                           ctypes.byref(coarse) if coarse else None,
+                                           ctypes.byref(n))
+    return st, n.value
+
+
+def test_select_workspace_size_layout():
+    p = hs.hs_select_params(32, 128, 512, 0, 145)
+    st, n = sel_size(p, kv_struct(), summ())
+    assert st == hs.HS_OK
+    assert n >= 4 * 8 * 4096 * 4          # one fp32 score per block and unit
+    assert n % 256 == 0
+    # two-level: coarse scores + kept coarse ids + fine candidate scores
+    kv4 = kv_struct(num_kv_heads=32, batch=8, max_pages=4096, page_size=64,
+                    num_phys_pages=8 * 4096, max_seq_len=262144)
+    p2 = hs.hs_select_params(32, 128, 512, 32, 137)
+    st, n2 = sel_size(p2, kv4, summ(hs.HS_SUMMARY_MEAN, 64, 4096),
+                      summ(hs.HS_SUMMARY_MEAN, 1024, 256))
+    assert st == hs.HS_OK
+    units = 8 * 32
+    assert n2 >= units * (256 * 4 + 32 * 4 + 4 + 512 * 4)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(head_dim=96), hs.HS_ERR_UNSUPPORTED),
+    (dict(dtype=7), hs.HS_ERR_UNSUPPORTED),
+    (dict(batch=0), hs.HS_ERR_INVALID_ARG),
+    (dict(page_table=0), hs.HS_ERR_INVALID_ARG),
+    (dict(seq_lens=0), hs.HS_ERR_INVALID_ARG),
+    (dict(max_seq_len=4096 * 32 + 1), hs.HS_ERR_INVALID_ARG),
+    (dict(page_size=0), hs.HS_ERR_INVALID_ARG),
+])
+def test_select_rejects_bad_cache(change, code):
+    p = hs.hs_select_params(32, 128, 512, 0, 145)
+    assert sel_size(p, kv_struct(**change), summ())[0] == code
+
+
+@pytest.mark.parametrize("params,code", [
+    ((30, 128, 512, 0, 145), hs.HS_ERR_INVALID_ARG),   # Hq not a multiple of Hkv
+    ((24, 128, 512, 0, 145), hs.HS_ERR_UNSUPPORTED),   # G = 3
+    ((32, 128, 512, 0, 144), hs.HS_ERR_INVALID_ARG),   # capacity below k + W/S + 1
+    ((32, -1, 512, 0, 145), hs.HS_ERR_INVALID_ARG),
+    ((32, 128, -5, 0, 145), hs.HS_ERR_INVALID_ARG),
+])
+def test_select_rejects_bad_params(params, code):
+    assert sel_size(hs.hs_select_params(*params), kv_struct(), summ())[0] == code
+
+
+def test_select_rejects_bad_summaries():
+    p = hs.hs_select_params(32, 128, 512, 0, 145)
+    assert sel_size(p, kv_struct(), summ(max_blocks=4095))[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(p, kv_struct(), summ(data=FAKE + 1))[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(p, kv_struct(), summ(kind=5))[0] == hs.HS_ERR_INVALID_ARG
+    # two-level needs a coarse table whose block size is a multiple of S
+    p2 = hs.hs_select_params(32, 128, 512, 8, 145)
+    assert sel_size(p2, kv_struct(), summ())[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(p2, kv_struct(), summ(), summ(hs.HS_SUMMARY_MEAN, 48, 4096))[0] == \
+        hs.HS_ERR_INVALID_ARG
+    assert sel_size(p2, kv_struct(), summ(), summ(hs.HS_SUMMARY_MEAN, 1024, 128))[0] == hs.HS_OK
+
+
+def test_entry_points_fail_before_launch():
+    L = hs.lib()
+    kv = kv_struct()
+    p = hs.hs_select_params(32, 128, 512, 0, 145)
+    fine = summ()
+    st, need = sel_size(p, kv, fine)
+    assert st == hs.HS_OK
+    # workspace too small / missing -> HS_ERR_WORKSPACE, nothing launched
+    assert L.hs_select_blocks(ctypes.byref(p), ctypes.byref(kv), FAKE, ctypes.byref(fine), None,
+                              FAKE, FAKE, FAKE, need - 1, None) == hs.HS_ERR_WORKSPACE
+    assert L.hs_select_blocks(ctypes.byref(p), ctypes.byref(kv), FAKE, ctypes.byref(fine), None,
+                              FAKE, FAKE, None, need, None) == hs.HS_ERR_WORKSPACE
+    assert L.hs_select_blocks(ctypes.byref(p), ctypes.byref(kv), None, ctypes.byref(fine), None,
+                              FAKE, FAKE, FAKE, need, None) == hs.HS_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert L.hs_decode_workspace_size(ctypes.byref(kv), 32, 32, 145, ctypes.byref(n)) == hs.HS_OK
+    dneed = n.value
+    # 4 * 8 units * ceil(145 / 8) splits * 4 heads * (128 + 2) floats
+    assert dneed >= 32 * 19 * 4 * 130 * 4
+    args = (ctypes.byref(kv), FAKE, 32, ctypes.c_float(0.0), 32, FAKE, FAKE, 145, FAKE)
+    assert L.hs_sparse_decode(*args, FAKE, dneed - 1, None) == hs.HS_ERR_WORKSPACE
+    assert L.hs_sparse_decode(ctypes.byref(kv), FAKE, 32, ctypes.c_float(float("nan")), 32, FAKE,
+                              FAKE, 145, FAKE, FAKE, dneed, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_sparse_decode(ctypes.byref(kv), FAKE, 32, ctypes.c_float(0.0), 0, FAKE, FAKE,
+                              145, FAKE, FAKE, dneed, None) == hs.HS_ERR_INVALID_ARG
+    kv_nov = kv_struct(v_pool=0)
+    assert L.hs_sparse_decode(ctypes.byref(kv_nov), FAKE, 32, ctypes.c_float(0.0), 32, FAKE, FAKE,
+                              145, FAKE, FAKE, dneed, None) == hs.HS_ERR_INVALID_ARG
+    # build: bad block_begin, missing K pool, misaligned pool
+    assert L.hs_build_summaries(ctypes.byref(kv), -1, ctypes.byref(fine), None) == \
+        hs.HS_ERR_INVALID_ARG
+    kv_nok = kv_struct(k_pool=0)
+    assert L.hs_build_summaries(ctypes.byref(kv_nok), 0, ctypes.byref(fine), None) == \
+        hs.HS_ERR_INVALID_ARG
+    kv_mis = kv_struct(k_pool=FAKE + 2)
+    assert L.hs_build_summaries(ctypes.byref(kv_mis), 0, ctypes.byref(fine), None) == \
+        hs.HS_ERR_INVALID_ARG
+    assert L.hs_build_summaries(None, 0, ctypes.byref(fine), None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_select_workspace_size(None, ctypes.byref(kv), ctypes.byref(fine), None,
+                                      ctypes.byref(n)) == hs.HS_ERR_INVALID_ARG

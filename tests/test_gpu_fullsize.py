@@ -1,0 +1,104 @@
+"""GPU parity at the five workloads' full sizes, on sampled units.
+
+The whole problem runs on the GPU through the C ABI, in the launch
+configuration the benchmark times; the oracle recomputes a few units one by
+one from regenerated inputs (the generator is counter-based, so any unit's
+rows can be drawn alone). Ids follow the near-tie rule, outputs the per-row
+relative bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (Problem, check_ids, check_rows, log, magnitudes, oracle_select,
+                         unit_inputs)
+from synth.workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_units(w, n):
+    all_units = [(b, g) for b in range(w.batch) for g in range(w.hkv)]
+    idx = np.unique(np.linspace(0, len(all_units) - 1, n).round().astype(int))
+    return [all_units[i] for i in idx]
+
+
+def check_units(w, P, q_step, ids, cnt, outs, units, step=0):
+    ties = 0
+    for b, g in units:
+        T = w.T
+        qo, K, V = unit_inputs(w, 0, b, g, step)
+        sel = oracle_select(w, qo, K, T)
+        gi = ids[b, g, :cnt[b, g]]
+        ties += check_ids(w, gi, sel, magnitudes(w, qo, K, T), T,
+                          what="config %d unit (%d,%d)" % (w.config, b, g))
+        for layer, out in enumerate(outs):
+            if layer:
+                qo, K, V = unit_inputs(w, layer, b, g, step)
+            ref = oracle.attend_unit(qo, K, V, T, gi, w.S)
+            check_rows(w, out[b, g * w.G:(g + 1) * w.G], ref,
+                       "config %d layer %d unit (%d,%d)" % (w.config, layer, b, g))
+    return ties
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_single_layer(cfg):
+    w = CONFIGS[cfg]
+    log("config %d (%s): generating and uploading inputs" % (cfg, w.name))
+    P = Problem.make(w)
+    q = P.q()
+    summ = P.summaries()
+    ids_t, cnt_t = P.select(q, summ)
+    out = P.decode(q, ids_t, cnt_t)
+    torch.cuda.synchronize()
+    log("config %d: GPU step done; oracle on sampled units" % cfg)
+    ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+    assert np.all(cnt > 0) and np.all(cnt <= w.max_selected)
+    outs = [out.cpu().double().numpy()]
+    ties = check_units(w, P, q, ids, cnt, outs, sample_units(w, 4 if cfg > 1 else 4))
+    # needle recall (reported, not asserted): needle blocks kept by the selection
+    if w.needles:
+        hit = tot = 0
+        for b, g in sample_units(w, 8):
+            nb = set(w.needle_blocks(b, g).tolist())
+            tot += len(nb)
+            hit += len(nb & set(ids[b, g, :cnt[b, g]].tolist()))
+        log("config %d: needle recall %d/%d on 8 sampled units" % (cfg, hit, tot))
+    log("config %d: %d tolerated near-tie differences; mean count %.1f" % (cfg, ties, cnt.mean()))
+    del P
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_shared_selection_drift():
+    """Config 5: 8 layers share the layer-0 selection; 16 drift steps. Every
+    step's selection is computed on the GPU; the first and the last step are
+    checked against the oracle on sampled units (ids, and all 8 layers'
+    outputs); the per-step set difference is reported."""
+    w = CONFIGS[5]
+    log("config 5: generating and uploading %d layers" % w.layers)
+    P = Problem.make(w, layers=w.layers)
+    summ = P.summaries(0)
+    prev = None
+    diffs = []
+    units = sample_units(w, 3)
+    for step in range(w.steps):
+        q0 = P.q(0, step)
+        ids_t, cnt_t = P.select(q0, summ)
+        ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+        if prev is not None:
+            d = [len(set(ids[b, g, :cnt[b, g]]) - set(prev[0][b, g, :prev[1][b, g]]))
+                 for b in range(w.batch) for g in range(w.hkv)]
+            diffs.append((min(d), float(np.mean(d)), max(d)))
+        prev = (ids, cnt)
+        if step in (0, w.steps - 1):
+            outs = [P.decode(P.q(layer, step), ids_t, cnt_t, layer=layer).cpu().double().numpy()
+                    for layer in range(w.layers)]
+            log("config 5 step %d: checking %d units x %d layers" % (step, len(units), w.layers))
+            check_units(w, P, q0, ids, cnt, outs, units, step=step)
+    log("config 5: |S_t minus S_t-1| per step (min, mean, max): %s" %
+        ", ".join("(%d, %.1f, %d)" % x for x in diffs))
+    del P
+    torch.cuda.empty_cache()
