@@ -243,8 +243,10 @@ def hs_version() -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A uint8 device buffer of at least nbytes (256-byte aligned by torch)."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A zero-filled uint8 device buffer of at least nbytes (256-byte aligned
+    by torch). Workspaces must be zero before their first use (they hold
+    arrival counters that every call leaves at zero)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 class Prepared:

@@ -76,10 +76,12 @@ int group_size(const hs_kv_cache* kv, int32_t num_q_heads, hs_status* st) {
 }
 
 // Workspace of hs_select_blocks (byte offsets).
+// Workspace of hs_select_blocks: [arrival counters, 2 levels][coarse scores]
+// [kept coarse ids][their counts][fine scores].
 struct SelectLayout {
   bool two_level;
   int64_t units, nb_fine, nc, kc_cap, ratio, fine_slots;
-  size_t off_coarse_scores, off_gamma, off_gamma_cnt, off_fine_scores, total;
+  size_t off_cnt, off_coarse_scores, off_gamma, off_gamma_cnt, off_fine_scores, total;
 };
 
 hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
@@ -108,7 +110,8 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
   L->two_level = two;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->nb_fine = nb > 0 ? nb : 1;
-  size_t off = 0;
+  L->off_cnt = 0;
+  size_t off = align_up(sizeof(int32_t) * 2 * L->units);
   if (two) {
     L->nc = std::max<int64_t>(1, blocks_needed(kv, coarse->block_size));
     L->kc_cap = std::min<int64_t>(p->top_k_coarse, L->nc);
@@ -132,9 +135,10 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
   return HS_OK;
 }
 
+// Workspace of hs_sparse_decode: [arrival counters][split partials o][(m, l)].
 struct DecodeLayout {
   int64_t units, bps, max_splits, G;
-  size_t off_o, off_ml, total;
+  size_t off_cnt, off_o, off_ml, total;
 };
 
 hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block_size,
@@ -146,11 +150,12 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
   if (block_size < 1 || max_selected < 1) return HS_ERR_INVALID_ARG;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->G = G;
-  L->bps = hs::decode_blocks_per_split(block_size);
+  L->bps = hs::decode_blocks_per_split(block_size, max_selected);
   L->max_splits = ceil_div(max_selected, L->bps);
   if (L->max_splits > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
-  L->off_o = 0;
-  L->off_ml = align_up(sizeof(float) * L->units * L->max_splits * G * kv->head_dim);
+  L->off_cnt = 0;
+  L->off_o = align_up(sizeof(int32_t) * L->units);
+  L->off_ml = align_up(L->off_o + sizeof(float) * L->units * L->max_splits * G * kv->head_dim);
   L->total = align_up(L->off_ml + sizeof(float) * L->units * L->max_splits * G * 2);
   return HS_OK;
 }
@@ -221,20 +226,15 @@ hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, c
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int G = prm->num_q_heads / kv->num_kv_heads;
-  const KvView view = view_of(kv);
-
-  hs::ScoreParams sp;
-  sp.kv = view;
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+  hs::SelectParams sp;
+  sp.kv = view_of(kv);
   sp.q = q;
-  sp.G = G;
-  hs::TopkParams tp;
-  tp.kv = view;
+  sp.G = prm->num_q_heads / kv->num_kv_heads;
   hipError_t e;
   int32_t* gamma = nullptr;
   int32_t* gamma_cnt = nullptr;
   if (L.two_level) {
-    float* cs = reinterpret_cast<float*>(ws + L.off_coarse_scores);
     gamma = reinterpret_cast<int32_t*>(ws + L.off_gamma);
     gamma_cnt = reinterpret_cast<int32_t*>(ws + L.off_gamma_cnt);
     sp.summ = coarse->data;
@@ -246,24 +246,16 @@ hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, c
     sp.gamma_cap = 0;
     sp.ratio = 1;
     sp.n_slots_max = (int32_t)L.nc;
-    sp.scores = cs;
-    if ((e = hs::launch_scores(sp, s)) != hipSuccess) return from_hip(e);
-    tp.scores = cs;
-    tp.n_slots_max = (int32_t)L.nc;
-    tp.block_size = coarse->block_size;
-    tp.top_k = prm->top_k_coarse;
-    tp.window = 0;
-    tp.gamma = nullptr;
-    tp.gamma_cnt = nullptr;
-    tp.gamma_cap = 0;
-    tp.ratio = 1;
-    tp.out_ids = gamma;
-    tp.out_cnt = gamma_cnt;
-    tp.out_cap = (int32_t)L.kc_cap;
-    tp.out_blocks_max = (int32_t)L.nc;
-    if ((e = hs::launch_topk(tp, s)) != hipSuccess) return from_hip(e);
+    sp.scores = reinterpret_cast<float*>(ws + L.off_coarse_scores);
+    sp.top_k = prm->top_k_coarse;
+    sp.window = 0;
+    sp.out_ids = gamma;
+    sp.out_cnt = gamma_cnt;
+    sp.out_cap = (int32_t)L.kc_cap;
+    sp.out_blocks_max = (int32_t)L.nc;
+    sp.counters = counters + L.units;
+    if ((e = hs::launch_select(sp, s)) != hipSuccess) return from_hip(e);
   }
-  float* fs = reinterpret_cast<float*>(ws + L.off_fine_scores);
   sp.summ = fine->data;
   sp.kind = fine->kind;
   sp.block_size = fine->block_size;
@@ -273,22 +265,15 @@ hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, c
   sp.gamma_cap = (int32_t)L.kc_cap;
   sp.ratio = (int32_t)L.ratio;
   sp.n_slots_max = (int32_t)L.fine_slots;
-  sp.scores = fs;
-  if ((e = hs::launch_scores(sp, s)) != hipSuccess) return from_hip(e);
-  tp.scores = fs;
-  tp.n_slots_max = (int32_t)L.fine_slots;
-  tp.block_size = fine->block_size;
-  tp.top_k = prm->top_k;
-  tp.window = prm->window_tokens;
-  tp.gamma = gamma;
-  tp.gamma_cnt = gamma_cnt;
-  tp.gamma_cap = (int32_t)L.kc_cap;
-  tp.ratio = (int32_t)L.ratio;
-  tp.out_ids = block_ids;
-  tp.out_cnt = num_selected;
-  tp.out_cap = prm->max_selected;
-  tp.out_blocks_max = (int32_t)L.nb_fine;
-  return from_hip(hs::launch_topk(tp, s));
+  sp.scores = reinterpret_cast<float*>(ws + L.off_fine_scores);
+  sp.top_k = prm->top_k;
+  sp.window = prm->window_tokens;
+  sp.out_ids = block_ids;
+  sp.out_cnt = num_selected;
+  sp.out_cap = prm->max_selected;
+  sp.out_blocks_max = (int32_t)L.nb_fine;
+  sp.counters = counters;
+  return from_hip(hs::launch_select(sp, s));
 }
 
 hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q, int32_t num_q_heads, float scale,
@@ -316,6 +301,7 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q, int32_t num_q_h
   p.max_splits = (int32_t)L.max_splits;
   p.part_o = reinterpret_cast<float*>(ws + L.off_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
+  p.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
   p.out = out;
   return from_hip(hs::launch_decode(p, static_cast<hipStream_t>(stream)));
 }

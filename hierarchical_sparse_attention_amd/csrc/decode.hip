@@ -7,44 +7,374 @@
 // compact copy); "SparDA" article section 3.3 (only the selected pages are
 // read) and section 3.4 (one block list shared by every layer).
 //
-// k_decode_split - grid (splits, units). A workgroup owns a run of
-//   blocks_per_split consecutive entries of a unit's id list (about 256
-//   tokens) and computes, for the unit's G query heads, an fp32 online-softmax
-//   partial (m, l, o) over them. Each wave takes every fourth entry. A token
-//   row is read by LPT lanes with one 16-byte load each, so one wave
-//   instruction covers TPW tokens; K and V loads for UNR such instructions
-//   are issued before any use. The q.k dot is reduced across the LPT lanes
-//   with DPP, which leaves the logit in every lane of the token's lane group:
-//   each lane then accumulates p * v for its own head_dim slice without any
-//   broadcast. Token groups, then waves, are merged at the end (LSE rule).
-// k_decode_merge - one workgroup per (b, query head): log-sum-exp merge of
-//   the unit's split partials into the fp32 output.
-// Logits are kept in base 2: q is pre-multiplied by scale * log2(e), so
-// exp(l - m) = exp2(l2 - m2) exactly in real arithmetic.
+// Work split: grid (splits, units). A workgroup of 4 waves owns a run of
+// blocks_per_split consecutive entries of a unit's id list; each wave takes
+// every fourth entry and keeps an fp32 online-softmax state (m, l, o) for
+// the unit's G query heads. The workgroup combines its waves in LDS, writes
+// one partial per split, and the last workgroup of the unit to finish
+// (arrival counter in the workspace) merges the unit's partials into the
+// output with the log-sum-exp rule, so one launch does the whole stage.
+//
+// k_decode_bf16 (bf16 caches): q.k on the matrix cores. For a 16-token tile
+// v_mfma_f32_16x16x32_bf16 takes the unit's query heads as rows of A (head j
+// in row 4 (j % 4) + j / 4, so every 16-lane group of the result holds one
+// head's 16 logits) and the K tile as B: each lane's 16-byte load of
+// 8 consecutive dims of one token is exactly its B operand, so K goes from
+// HBM to the MFMA without any shuffle. Softmax statistics are per head and
+// wave-uniform; p and the rescale factor go through a small per-wave LDS
+// slice to the p.v accumulation, which runs on the VALU in fp32 with V read
+// as 16-byte rows (lane: 8 dims of one token).
+// k_decode_f32 (float32 caches): all on the VALU; the q.k dot is reduced
+// across the lanes of a token row with DPP.
+// Logits are kept in base 2: the logit scale is multiplied by log2(e), so
+// exp(l - m) = exp2(l2 - m2) in real arithmetic.
 #include "hs_internal.h"
 
 namespace hs {
 namespace {
 
 constexpr int kDecWaves = 4;
+// The host keeps the number of splits of a unit at most kMaxSplits (it grows
+// blocks_per_split for very long id lists), so the merge's (m, l) table of
+// 2 * kMaxSplits * G floats fits in the 4 * G * D floats of the wave area.
+constexpr int kMaxSplits = 128;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-template <typename TE, int D, int G, int UNR>
-__global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
-  constexpr int EPL = Vec16<TE>::EPL;
-  constexpr int LPT = D / EPL;        // lanes per token row
-  constexpr int TPW = kWave / LPT;    // tokens per wave instruction
+template <int D, int G>
+struct SplitShared {
+  float o[kDecWaves][G][D];
+  float m[kDecWaves][G];
+  float l[kDecWaves][G];
+  int last;
+};
+
+__device__ __forceinline__ int clamp_count(const DecodeParams& p, int unit) {
+  int cnt = p.counts[unit];
+  return cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
+}
+
+// Combine the waves of this workgroup, publish the split's partial, and let
+// the unit's last-arriving workgroup merge all partials into `out`.
+template <int D, int G>
+__device__ void finish_split(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int split,
+                             int ns) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  const int64_t ps = (int64_t)unit * p.max_splits + split;
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    const int j = idx / D, dd = idx % D;
+    float mn = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mn = fmaxf(mn, sh.m[w][j]);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float a = exp2f(sh.m[w][j] - ms);
+      acc += sh.o[w][j][dd] * a;
+      lsum += sh.l[w][j] * a;
+    }
+    publish(&p.part_o[(ps * G + j) * D + dd], acc);
+    if (dd == 0) {
+      publish(&p.part_ml[(ps * G + j) * 2 + 0], mn);
+      publish(&p.part_ml[(ps * G + j) * 2 + 1], lsum);
+    }
+  }
+  if (!arrive_last(&p.counters[unit], ns, &sh.last)) return;
+  // Last workgroup of the unit: log-sum-exp merge of its ns <= kMaxSplits
+  // partials. Thread t < stride owns output elements t + r * stride of the
+  // unit's G x D block (r < R). The (m, l) loads and the first kMergeBatch
+  // partial-output loads are issued together, so for the usual split counts
+  // the whole merge costs one round trip to the device-coherent level.
+  constexpr int stride = G * D < 256 ? G * D : 256;
+  constexpr int R = G * D / stride;
+  constexpr int kMergeBatch = 80;
+  float* sm = &sh.o[0][0][0];                 // [ns][G] maxima, then weights
+  float* sl = sm + kMaxSplits * G;            // [ns][G] sums
+  const int64_t p0 = (int64_t)unit * p.max_splits;
+  const int npairs = ns * R;                  // (split, r) loads of this thread
+  const bool owner = tid < stride;
+  float mv = 0.f, lv = 0.f;
+  const bool ml_loader = tid < ns * G;
+  if (ml_loader) {
+    mv = published(&p.part_ml[(p0 * G + tid) * 2]);
+    lv = published(&p.part_ml[(p0 * G + tid) * 2 + 1]);
+  }
+  float v[kMergeBatch];
+#pragma unroll
+  for (int q = 0; q < kMergeBatch; ++q) {
+    const int qq = min(q, npairs - 1);  // unconditional (clamped) loads overlap
+    v[q] = published(&p.part_o[(p0 + qq / R) * G * D + (owner ? tid : 0) + (qq % R) * stride]);
+  }
+  for (int t = tid; t < ns * G; t += blockDim.x) {  // more than 256 (m, l) pairs
+    sm[t] = t == tid ? mv : published(&p.part_ml[(p0 * G + t) * 2]);
+    sl[t] = t == tid ? lv : published(&p.part_ml[(p0 * G + t) * 2 + 1]);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mn = -INFINITY;
+    for (int s = 0; s < ns; ++s) mn = fmaxf(mn, sm[s * G + tid]);
+    sh.m[0][tid] = mn == -INFINITY ? 0.f : mn;
+  }
+  __syncthreads();
+  for (int t = tid; t < ns * G; t += blockDim.x) sm[t] = exp2f(sm[t] - sh.m[0][t % G]);
+  __syncthreads();
+  if (tid < G) {
+    float lsum = 0.f;
+    for (int s = 0; s < ns; ++s) lsum += sl[s * G + tid] * sm[s * G + tid];
+    sh.l[0][tid] = lsum;
+  }
+  __syncthreads();
+  if (!owner) return;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMergeBatch; ++q)
+    if (q < npairs) acc[q % R] += v[q] * sm[(q / R) * G + (tid + (q % R) * stride) / D];
+  for (int q = kMergeBatch; q < npairs; ++q)  // long id lists only
+    acc[q % R] += published(&p.part_o[(p0 + q / R) * G * D + tid + (q % R) * stride]) *
+                  sm[(q / R) * G + (tid + (q % R) * stride) / D];
+  const int Hq = p.kv.num_kv_heads * G;
+  const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = tid + r * stride, j = idx / D;
+    const float lsum = sh.l[0][j];
+    p.out[((int64_t)b * Hq + g * G) * D + idx] = lsum > 0.f ? acc[r] / lsum : 0.f;
+  }
+}
+
+// An empty selection has no split to merge: its output rows are zero.
+template <int D, int G>
+__device__ void write_empty(const DecodeParams& p, int unit) {
+  const int Hq = p.kv.num_kv_heads * G;
+  const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x)
+    p.out[((int64_t)b * Hq + g * G) * D + idx] = 0.f;
+}
+
+// --------------------------------------------------------------- bf16 path
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
+  constexpr int KC = D / 32;       // MFMA k-chunks per token row
+  constexpr int VL = D / 8;        // lanes per V row (16 bytes each)
+  constexpr int TPV = kWave / VL;  // tokens per V load instruction
+  constexpr int NV = 32 / TPV;     // V loads per 32-token stage
+  constexpr int GR = (G + 3) / 4;  // MFMA result registers that carry heads
+  constexpr int EB = 2;            // bytes per element
+  __shared__ SplitShared<D, G> sh;
+  __shared__ float sp[kDecWaves][32][G];
+  __shared__ float salpha[kDecWaves][G];
+
   const KvView& kv = p.kv;
   const int unit = blockIdx.y, split = blockIdx.x;
+  const int cnt = clamp_count(p, unit);
+  if (cnt == 0) {
+    if (split == 0) write_empty<D, G>(p, unit);
+    return;
+  }
+  const int bps = p.blocks_per_split;
+  const int e0 = split * bps;
+  if (e0 >= cnt) return;
+  const int e1 = min(e0 + bps, cnt), ns = (cnt + bps - 1) / bps;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int T = clamp_len(kv, b);
   const int S = p.block_size;
   const int nb = (T + S - 1) / S;
-  int cnt = p.counts[unit];
-  cnt = cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
-  const int e0 = split * p.blocks_per_split;
-  if (e0 >= cnt) return;  // no partial: the merge reads only splits below ceil(cnt / bps)
-  const int e1 = min(e0 + p.blocks_per_split, cnt);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int vt = lane / VL, vd = (lane % VL) * 8;
+  const int Hq = kv.num_kv_heads * G;
+  const float scale = p.scale_log2;
+  // stages are 32 tokens; they stay inside one page when both the page and the
+  // block sizes are multiples of 32, so a single page lookup serves the stage
+  const bool whole_page = (kv.page_size % 32 == 0) && (S % 32 == 0);
+  const int64_t row_bytes = (int64_t)D * EB;
 
+  // A operands: query head j in row 4 (j % 4) + j / 4 (zero rows elsewhere)
+  bf16x8_t aq[KC];
+  {
+    const int j = 4 * (r16 & 3) + (r16 >> 2);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
+                          ((int64_t)b * Hq + g * G + (j < G ? j : 0)) * row_bytes;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      uint4 r = j < G ? *reinterpret_cast<const uint4*>(qrow + (32 * c + 8 * grp) * EB)
+                      : make_uint4(0, 0, 0, 0);
+      aq[c] = __builtin_bit_cast(bf16x8_t, r);
+    }
+  }
+  float m_run[GR], l_run[GR], o[G][8];
+#pragma unroll
+  for (int i = 0; i < GR; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
+
+  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
+  for (int e = e0 + wave; e < e1; e += kDecWaves) {
+    const int beta = ids[e];
+    if ((unsigned)beta >= (unsigned)nb) continue;  // wave-uniform
+    const int tb = beta * S, te = min(tb + S, T);
+    for (int ts = tb; ts < te; ts += 32) {
+      uint4 kr[2][KC], vr[NV];
+      bool kok[2];
+      if (whole_page) {
+        const int page = kv.page_table[(int64_t)b * kv.max_pages + ts / kv.page_size];
+        const bool pok = (unsigned)page < (unsigned)kv.num_phys_pages;
+        const int64_t base =
+            pok ? (((int64_t)page * kv.num_kv_heads + g) * kv.page_size + ts % kv.page_size) *
+                      row_bytes
+                : 0;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const int t = ts + 16 * tau + r16;
+          kok[tau] = pok && t < te;
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            kr[tau][c] = kok[tau] ? *reinterpret_cast<const uint4*>(
+                                        kv.k_pool + base + (16 * tau + r16) * row_bytes +
+                                        (32 * c + 8 * grp) * EB)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int tt = TPV * u + vt;
+          vr[u] = (pok && ts + tt < te)
+                      ? *reinterpret_cast<const uint4*>(kv.v_pool + base + tt * row_bytes + vd * EB)
+                      : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const int t = ts + 16 * tau + r16;
+          const int64_t off = t < te ? row_offset(kv, b, g, t) : -1;
+          kok[tau] = off >= 0;
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            kr[tau][c] = kok[tau] ? *reinterpret_cast<const uint4*>(kv.k_pool + off +
+                                                                    (32 * c + 8 * grp) * EB)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int t = ts + TPV * u + vt;
+          const int64_t off = t < te ? row_offset(kv, b, g, t) : -1;
+          vr[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB)
+                           : make_uint4(0, 0, 0, 0);
+        }
+      }
+      // q.k for the two 16-token tiles
+      f32x4_t acc[2];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        acc[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              aq[c], __builtin_bit_cast(bf16x8_t, kr[tau][c]), acc[tau], 0, 0, 0);
+      }
+      // online softmax; register i of lane (grp, r16) holds head 4 i + grp
+#pragma unroll
+      for (int i = 0; i < GR; ++i) {
+        const float x0 = kok[0] ? acc[0][i] * scale : -INFINITY;
+        const float x1 = kok[1] ? acc[1][i] * scale : -INFINITY;
+        const float mx = group_max<16>(fmaxf(x0, x1));
+        const float mn = fmaxf(m_run[i], mx);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(m_run[i] - ms);
+        const float p0 = exp2f(x0 - ms), p1 = exp2f(x1 - ms);
+        l_run[i] = l_run[i] * alpha + p0 + p1;
+        m_run[i] = mn;
+        const int j = 4 * i + grp;
+        if (j < G) {
+          sp[wave][r16][j] = p0;
+          sp[wave][16 + r16][j] = p1;
+          if (r16 == 0) salpha[wave][j] = alpha;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // p.v on the VALU: lane (vt, vd) accumulates its tokens into dims vd..vd+7
+      float al[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) al[j] = salpha[wave][j];
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[j][k] *= al[j];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        float vf[8];
+        Vec16<bf16_t>::unpack(vr[u], vf);
+        const int tt = TPV * u + vt;
+        float pj[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) pj[j] = sp[wave][tt][j];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[j][k] = fmaf(pj[j], vf[k], o[j][k]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // the running max is uniform per head across the wave, so the token groups'
+  // partial sums add without rescaling
+#pragma unroll
+  for (int s = VL; s < kWave; s *= 2)
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[j][k] += __shfl_xor(o[j][k], s);
+#pragma unroll
+  for (int i = 0; i < GR; ++i) l_run[i] = group_sum<16>(l_run[i]);
+  if (lane < VL) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sh.o[wave][j][vd + k] = o[j][k];
+  }
+  if (r16 == 0) {
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      const int j = 4 * i + grp;
+      if (j < G) {
+        sh.m[wave][j] = m_run[i];
+        sh.l[wave][j] = l_run[i];
+      }
+    }
+  }
+  finish_split<D, G>(p, sh, unit, split, ns);
+}
+
+// -------------------------------------------------------------- float32 path
+template <int D, int G, int UNR>
+__global__ __launch_bounds__(256) void k_decode_f32(DecodeParams p) {
+  constexpr int EPL = 4;              // floats per 16-byte load
+  constexpr int LPT = D / EPL;        // lanes per token row
+  constexpr int TPW = kWave / LPT;    // tokens per wave instruction
+  __shared__ SplitShared<D, G> sh;
+  const KvView& kv = p.kv;
+  const int unit = blockIdx.y, split = blockIdx.x;
+  const int cnt = clamp_count(p, unit);
+  if (cnt == 0) {
+    if (split == 0) write_empty<D, G>(p, unit);
+    return;
+  }
+  const int bps = p.blocks_per_split;
+  const int e0 = split * bps;
+  if (e0 >= cnt) return;
+  const int e1 = min(e0 + bps, cnt), ns = (cnt + bps - 1) / bps;
+  const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
+  const int T = clamp_len(kv, b);
+  const int S = p.block_size;
+  const int nb = (T + S - 1) / S;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int tg = lane / LPT, li = lane % LPT;
   const int Hq = kv.num_kv_heads * G;
@@ -52,13 +382,13 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
   float qv[G][EPL];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
-                        ((int64_t)b * Hq + g * G + j) * D * (int64_t)sizeof(TE) + li * 16;
-    Vec16<TE>::unpack(*reinterpret_cast<const uint4*>(qp), qv[j]);
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) qv[j][k] *= p.scale_log2;
+    const float4 r = *reinterpret_cast<const float4*>(
+        reinterpret_cast<const float*>(p.q) + ((int64_t)b * Hq + g * G + j) * D + li * EPL);
+    qv[j][0] = r.x * p.scale_log2;
+    qv[j][1] = r.y * p.scale_log2;
+    qv[j][2] = r.z * p.scale_log2;
+    qv[j][3] = r.w * p.scale_log2;
   }
-
   float m[G], l[G], o[G][EPL];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -67,7 +397,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < EPL; ++k) o[j][k] = 0.f;
   }
-
   const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
   for (int e = e0 + wave; e < e1; e += kDecWaves) {
     const int beta = ids[e];
@@ -90,7 +419,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         float kf[EPL];
-        Vec16<TE>::unpack(kr[u], kf);
+        Vec16<float>::unpack(kr[u], kf);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           float a = 0.f;
@@ -107,23 +436,22 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 #pragma unroll
         for (int u = 1; u < UNR; ++u) mx = fmaxf(mx, x[u][j]);
         const float mn = fmaxf(m[j], mx);
-        // mn == -inf: nothing valid in this lane group yet; keep the state
         const float ms = mn == -INFINITY ? 0.f : mn;
-        const float alpha = exp2f(m[j] - ms);  // m = -inf -> 0
+        const float alpha = exp2f(m[j] - ms);
         m[j] = mn;
         l[j] *= alpha;
 #pragma unroll
         for (int k = 0; k < EPL; ++k) o[j][k] *= alpha;
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          pr[u][j] = exp2f(x[u][j] - ms);  // x = -inf -> 0
+          pr[u][j] = exp2f(x[u][j] - ms);
           l[j] += pr[u][j];
         }
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         float vf[EPL];
-        Vec16<TE>::unpack(vr[u], vf);
+        Vec16<float>::unpack(vr[u], vf);
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -131,8 +459,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
       }
     }
   }
-
-  // merge the TPW token groups of the wave (lanes LPT, 2 LPT, ... apart)
+  // merge the token groups of the wave (their running maxima differ)
 #pragma unroll
   for (int s = LPT; s < kWave; s *= 2) {
 #pragma unroll
@@ -151,104 +478,59 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
       }
     }
   }
-
-  // merge the waves through LDS and write this split's partial
-  __shared__ float sh_o[kDecWaves][G][D];
-  __shared__ float sh_m[kDecWaves][G], sh_l[kDecWaves][G];
   if (tg == 0) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) sh_o[wave][j][li * EPL + k] = o[j][k];
+      for (int k = 0; k < EPL; ++k) sh.o[wave][j][li * EPL + k] = o[j][k];
       if (li == 0) {
-        sh_m[wave][j] = m[j];
-        sh_l[wave][j] = l[j];
+        sh.m[wave][j] = m[j];
+        sh.l[wave][j] = l[j];
       }
     }
   }
-  __syncthreads();
-  const int64_t ps = (int64_t)unit * p.max_splits + split;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int j = idx / D, dd = idx % D;
-    float mn = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) mn = fmaxf(mn, sh_m[w][j]);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float a = exp2f(sh_m[w][j] - ms);
-      acc += sh_o[w][j][dd] * a;
-      lsum += sh_l[w][j] * a;
-    }
-    p.part_o[(ps * G + j) * D + dd] = acc;
-    if (dd == 0) {
-      p.part_ml[(ps * G + j) * 2 + 0] = mn;
-      p.part_ml[(ps * G + j) * 2 + 1] = lsum;
-    }
-  }
+  finish_split<D, G>(p, sh, unit, split, ns);
 }
 
 template <int D>
-__global__ __launch_bounds__(128) void k_decode_merge(DecodeParams p) {
-  const KvView& kv = p.kv;
-  const int Hq = kv.num_kv_heads * p.G;
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
-  const int g = h / p.G, j = h % p.G;
-  const int unit = b * kv.num_kv_heads + g;
-  int cnt = p.counts[unit];
-  cnt = cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
-  const int ns = (cnt + p.blocks_per_split - 1) / p.blocks_per_split;
-  const int64_t p0 = (int64_t)unit * p.max_splits;
-  float mn = -INFINITY;
-  for (int s = 0; s < ns; ++s) mn = fmaxf(mn, p.part_ml[((p0 + s) * p.G + j) * 2]);
-  const float ms = mn == -INFINITY ? 0.f : mn;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float acc = 0.f, lsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const int64_t r = (p0 + s) * p.G + j;
-      const float a = exp2f(p.part_ml[r * 2] - ms);
-      acc += p.part_o[r * D + dd] * a;
-      lsum += p.part_ml[r * 2 + 1] * a;
-    }
-    p.out[((int64_t)b * Hq + h) * D + dd] = lsum > 0.f ? acc / lsum : 0.f;
+hipError_t launch_bf16(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((k_decode_bf16<D, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_decode_bf16<D, 2>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_decode_bf16<D, 4>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_decode_bf16<D, 8>), grid, dim3(256), 0, s, p); break;
   }
+  return hipGetLastError();
 }
 
-template <typename TE, int D>
-hipError_t launch_split(const DecodeParams& p, dim3 grid, hipStream_t s) {
+template <int D>
+hipError_t launch_f32(const DecodeParams& p, dim3 grid, hipStream_t s) {
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_decode_split<TE, D, 1, 8>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_decode_split<TE, D, 2, 8>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_decode_split<TE, D, 4, 8>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_decode_split<TE, D, 8, 4>), grid, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_decode_f32<D, 1, 8>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_decode_f32<D, 2, 8>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_decode_f32<D, 4, 8>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_decode_f32<D, 8, 4>), grid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_blocks_per_split(int block_size) {
-  const int bps = 256 / block_size;
-  return bps < 1 ? 1 : bps;
+// Each of the 4 waves of a workgroup takes one block (several when blocks
+// are short), so a workgroup reads about 4 * max(S, 32) tokens; long id
+// lists get more blocks per split so that a unit has at most kMaxSplits.
+int decode_blocks_per_split(int block_size, int max_selected) {
+  int bps = block_size >= 32 ? 4 : 4 * ((32 + block_size - 1) / block_size);
+  const int need = (max_selected + kMaxSplits - 1) / kMaxSplits;
+  if (bps < need) bps = (need + 3) / 4 * 4;
+  return bps;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  const int units = p.kv.batch * p.kv.num_kv_heads;
-  dim3 grid(p.max_splits, units);
-  const bool bf = p.kv.elem_bytes == 2;
-  hipError_t e;
-  if (p.kv.head_dim == 64)
-    e = bf ? launch_split<bf16_t, 64>(p, grid, s) : launch_split<float, 64>(p, grid, s);
-  else
-    e = bf ? launch_split<bf16_t, 128>(p, grid, s) : launch_split<float, 128>(p, grid, s);
-  if (e != hipSuccess) return e;
-  const dim3 mgrid(p.kv.batch * p.kv.num_kv_heads * p.G);
-  if (p.kv.head_dim == 64)
-    hipLaunchKernelGGL(k_decode_merge<64>, mgrid, dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_decode_merge<128>, mgrid, dim3(128), 0, s, p);
-  return hipGetLastError();
+  const dim3 grid(p.max_splits, p.kv.batch * p.kv.num_kv_heads);
+  if (p.kv.elem_bytes == 2)
+    return p.kv.head_dim == 64 ? launch_bf16<64>(p, grid, s) : launch_bf16<128>(p, grid, s);
+  return p.kv.head_dim == 64 ? launch_f32<64>(p, grid, s) : launch_f32<128>(p, grid, s);
 }
 
 }  // namespace hs

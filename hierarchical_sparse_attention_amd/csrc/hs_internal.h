@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/hs_attn.h"
+#include "hs_attn.h"
 
 namespace hs {
 
@@ -92,6 +92,35 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// ------------------------------------------- cross-workgroup hand-off
+// Data that another workgroup of the same launch reads (split partials,
+// block scores) is written and read with relaxed device-scope atomic accesses:
+// on gfx950 they are plain loads and stores with the sc1 bit, which makes them
+// coherent across the per-XCD L2 caches without writing back or invalidating
+// a whole L2 (what a device-scope fence costs). A workgroup drains its stores
+// (s_waitcnt vmcnt(0)) and synchronises before one lane increments the
+// arrival counter; the workgroup that sees the last arrival then reads the
+// published data with device-scope loads.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float published(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every thread calls this; returns true in every thread of the workgroup that
+// arrived last (of `expected`) on `counter`, which it then resets to zero.
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int expected, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's published stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == expected - 1;
+    if (*flag) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag;
+}
+
 // ------------------------------------------------------------- cache access
 struct KvView {
   const uint8_t* k_pool;
@@ -124,10 +153,11 @@ struct SummParams {
 };
 hipError_t launch_build_summaries(const SummParams& p, hipStream_t s);
 
-struct ScoreParams {
+// One selection level (fused scoring + top-k + window).
+struct SelectParams {
   KvView kv;                 // shapes + seq_lens
   const void* q;             // [B][Hq][d]
-  const void* summ;          // summary table
+  const void* summ;          // summary table of this level
   int32_t kind, block_size, max_blocks;
   int32_t G;
   // candidate slots: single level -> slot c is block c (n_slots = ceil(T_b/S));
@@ -137,25 +167,16 @@ struct ScoreParams {
   int32_t gamma_cap, ratio;  // R = C / S
   int32_t n_slots_max;       // scores row length
   float* scores;             // [units][n_slots_max]
-};
-hipError_t launch_scores(const ScoreParams& p, hipStream_t s);
-
-struct TopkParams {
-  KvView kv;
-  const float* scores;       // [units][n_slots_max]
-  int32_t n_slots_max;
-  int32_t block_size;        // S of the output ids (fine) or C (coarse)
   int32_t top_k;
   int32_t window;            // tokens (0 = none)
-  const int32_t* gamma;      // two-level fine: ascending coarse ids, else null
-  const int32_t* gamma_cnt;
-  int32_t gamma_cap, ratio;
   int32_t* out_ids;          // [units][out_cap]
   int32_t* out_cnt;          // [units]
   int32_t out_cap;
-  int32_t out_blocks_max;    // blocks of the output level per unit (bitmap bits)
+  int32_t out_blocks_max;    // blocks of this level per unit (bitmap bits)
+  int32_t* counters;         // [units] workgroup arrivals; zero between calls
 };
-hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max);
 
 struct DecodeParams {
   KvView kv;
@@ -169,11 +190,12 @@ struct DecodeParams {
   int32_t blocks_per_split, max_splits;
   float* part_o;             // [units][max_splits][G][d]
   float* part_ml;            // [units][max_splits][G][2]
+  int32_t* counters;         // [units] split arrivals; zero between calls
   float* out;                // [B][Hq][d]
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-int decode_blocks_per_split(int block_size);
+int decode_blocks_per_split(int block_size, int max_selected);
 
-constexpr int kMaxBlocks = 1 << 20;  // blocks per unit a selection level may have
+constexpr int kMaxBlocks = 32768;  // blocks per unit of a summary level (LDS bitmap)
 
 }  // namespace hs

@@ -36,8 +36,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
  *     caller allocates and owns every buffer. The library allocates nothing,
- *     keeps no state between calls and is reentrant (two calls may run at the
- *     same time if they do not share output or workspace buffers).
+ *     keeps no host state between calls and is reentrant (two calls may run
+ *     at the same time if they do not share output or workspace buffers).
  *   - Struct arguments are read only during the call.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t, passed as
  *     void*; NULL = the default stream). Outputs are valid once the stream
@@ -119,7 +119,7 @@ typedef struct {
  *                 [..][0][i] = min_t k_t,i and [..][1][i] = max_t k_t,i over
  *                 the valid tokens of block beta, in the KV dtype (exact).
  *   block_size  : S (tokens per block), >= 1.
- *   max_blocks  : rows per unit, >= ceil(max_seq_len / S).
+ *   max_blocks  : rows per unit, >= ceil(max_seq_len / S) and <= 32768.
  * Rows at or beyond ceil(T_b / S) are left untouched by the build and never
  * read by the selection. */
 typedef struct {
@@ -191,7 +191,12 @@ hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin,
  *                  are left untouched)
  *   num_selected : int32[batch][Hkv]
  * Only shapes and seq_lens of `kv` are used (pools may be NULL).
- * workspace: device buffer of at least hs_select_workspace_size() bytes. */
+ * workspace: device buffer of at least hs_select_workspace_size() bytes,
+ *   16-byte aligned and ZERO-FILLED before its first use. It starts with
+ *   per-unit arrival counters (the last workgroup of a unit to finish scoring
+ *   runs that unit's top-k); every call returns them to zero, so a workspace
+ *   can be reused by later calls on the same stream but must not be shared by
+ *   calls that may run at the same time. */
 hs_status hs_select_blocks(const hs_select_params* p, const hs_kv_cache* kv,
                            const void* q, const hs_summaries* fine,
                            const hs_summaries* coarse, int32_t* block_ids,
@@ -211,8 +216,15 @@ hs_status hs_select_blocks(const hs_select_params* p, const hs_kv_cache* kv,
  *   block_size   : S of the ids (any S >= 1; need not equal page_size)
  *   out          : float32[batch][Hq][head_dim]
  * The same block_ids may be passed to the decode of every layer (shared
- * selection, [SparDA 3.4]); they are only read.
- * workspace: device buffer of at least hs_decode_workspace_size() bytes. */
+ * selection, [SparDA 3.4]); they are only read. Ids of one unit must be
+ * distinct (hs_select_blocks guarantees it); an id listed twice is attended
+ * twice.
+ * workspace: device buffer of at least hs_decode_workspace_size() bytes,
+ *   16-byte aligned and ZERO-FILLED before its first use. It starts with
+ *   per-unit arrival counters (the last split of a unit to finish merges the
+ *   unit's partial results); every call returns them to zero, so a workspace
+ *   can be reused by later calls on the same stream but must not be shared by
+ *   calls that may run at the same time. */
 hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
                            int32_t num_q_heads, float scale,
                            int32_t block_size, const int32_t* block_ids,
