@@ -47,10 +47,59 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--event-steps", type=int, default=50)
+    ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", choices=["step", "copy"], default="step",
+                    help="copy: plain device-to-device copy of known size (counter calibration)")
     return ap.parse_args()
+
+
+def source_digest(files):
+    """sha256 over the given sources (relative to the repository root)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = {
+    "hs_sparse_decode": ["hierarchical_sparse_attention_amd/csrc/decode.hip",
+                         "hierarchical_sparse_attention_amd/csrc/hs_internal.h"],
+    "hs_select_blocks": ["hierarchical_sparse_attention_amd/csrc/select.hip",
+                         "hierarchical_sparse_attention_amd/csrc/hs_internal.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of the kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def copy_mode(args):
+    """Plain device copy of a known size: 1 GiB read + 1 GiB written per call.
+    Run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to calibrate the counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "calls": args.steps,
+                      "GBps": 2 * n / dt / 1e9}), flush=True)
 
 
 def main():
@@ -59,6 +108,9 @@ def main():
         print("bench.py runs on one GPU only: the path is measured on one GPU's share of the "
               "work (--gpus %d was requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.mode == "copy":
+        copy_mode(args)
+        return
     import numpy as np
     import torch
 
@@ -129,21 +181,33 @@ def main():
             call()
 
     # ------------------------------------------------ per-call event timing
-    n_ev = args.event_steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    # Each entry point is captured as a graph of back-to-back launches, one per
+    # input copy, and timed with events on the launch stream: the average per
+    # launch is the kernel's duration plus the dispatch gap between graph nodes,
+    # comparable with the kernel trace of rocprofv3.
     with torch.cuda.stream(stream):
-        for i in range(5):
-            step(copies[i % len(copies)])
-        for i in range(n_ev):
-            c = copies[i % len(copies)]
-            evs[i][0].record(stream)
-            for j, call in enumerate(c["calls"]):
-                call()
-                evs[i][j + 1].record(stream)
+        for c in copies:  # fill every copy's ids (the decode's input)
+            step(c)
     torch.cuda.synchronize()
-    per_call = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
-                         for i in range(n_ev)])
-    call_ms = per_call.mean(axis=0)
+    call_ms = []
+    for j in range(3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in copies:
+                c["calls"][j]()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.event_steps)]
+        with torch.cuda.stream(stream):
+            g.replay()
+            for e0, e1 in evs:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        call_ms.append(float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(copies))
+        del g
+    call_ms = np.array(call_ms)
     log("per-call mean ms: refresh %.4f select %.4f decode %.4f" % tuple(call_ms))
 
     # ---------------------------------------------------------- graphs
@@ -244,9 +308,11 @@ def main():
                         "hs_select_blocks": sel_ms, "hs_sparse_decode": dec_ms},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": dom_bytes, "avg_ms": dom_ms},
+                     "traffic": measured_traffic(dominant, w.name),
+                     "bytes_per_launch": dom_bytes, "avg_ms": dom_ms},
         "select_roofline": {"achieved": bytes_select / (sel_ms * 1e-3) / 1e9,
-                            "bytes_per_launch": bytes_select, "avg_ms": sel_ms},
+                            "bytes_per_launch": bytes_select, "avg_ms": sel_ms,
+                            "traffic": measured_traffic("hs_select_blocks", w.name)},
         "summary_build": {"ms": build_avg, "GBps": build_bytes / build_avg / 1e6},
         "warm_ms_per_step_single_copy": warm_ms,
         "cpu_baseline": cpu,

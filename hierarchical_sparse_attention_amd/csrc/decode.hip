@@ -156,6 +156,16 @@ __device__ void write_empty(const DecodeParams& p, int unit) {
 }
 
 // --------------------------------------------------------------- bf16 path
+// One 32-token stage of K and V as loaded (two 16-token MFMA tiles of K in
+// B-operand layout, V as 16-byte rows).
+template <int D>
+struct StageRegs {
+  uint4 k[2][D / 32];
+  uint4 v[32 / (kWave / (D / 8))];
+};
+
+constexpr int kStagesPerChunk = kWave;  // stage-table entries filled per pass
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
   constexpr int KC = D / 32;       // MFMA k-chunks per token row
@@ -167,6 +177,8 @@ __global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
   __shared__ SplitShared<D, G> sh;
   __shared__ float sp[kDecWaves][32][G];
   __shared__ float salpha[kDecWaves][G];
+  __shared__ int64_t st_base[kDecWaves][kStagesPerChunk];  // see the stage table below
+  __shared__ int st_len[kDecWaves][kStagesPerChunk];
 
   const KvView& kv = p.kv;
   const int unit = blockIdx.y, split = blockIdx.x;
@@ -183,13 +195,14 @@ __global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
   const int T = clamp_len(kv, b);
   const int S = p.block_size;
   const int nb = (T + S - 1) / S;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r16 = lane & 15, grp = lane >> 4;
   const int vt = lane / VL, vd = (lane % VL) * 8;
   const int Hq = kv.num_kv_heads * G;
   const float scale = p.scale_log2;
-  // stages are 32 tokens; they stay inside one page when both the page and the
-  // block sizes are multiples of 32, so a single page lookup serves the stage
+  // a 32-token stage stays inside one page when the page and block sizes are
+  // multiples of 32: then one page lookup serves the whole stage
   const bool whole_page = (kv.page_size % 32 == 0) && (S % 32 == 0);
   const int64_t row_bytes = (int64_t)D * EB;
 
@@ -217,112 +230,135 @@ __global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
 
-  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
-  for (int e = e0 + wave; e < e1; e += kDecWaves) {
-    const int beta = ids[e];
-    if ((unsigned)beta >= (unsigned)nb) continue;  // wave-uniform
-    const int tb = beta * S, te = min(tb + S, T);
-    for (int ts = tb; ts < te; ts += 32) {
-      uint4 kr[2][KC], vr[NV];
-      bool kok[2];
-      if (whole_page) {
-        const int page = kv.page_table[(int64_t)b * kv.max_pages + ts / kv.page_size];
-        const bool pok = (unsigned)page < (unsigned)kv.num_phys_pages;
-        const int64_t base =
-            pok ? (((int64_t)page * kv.num_kv_heads + g) * kv.page_size + ts % kv.page_size) *
-                      row_bytes
-                : 0;
+  // Issue the loads of stage `st` of the table. Lanes of masked tokens load a
+  // valid row of the same stage instead (their logits are -inf, so their p is
+  // 0 and the finite V row adds nothing); an empty stage loads nothing.
+  auto issue = [&](int st, StageRegs<D>& R, int& len) {
+    len = st_len[wave][st];
+    if (len == 0) return;
+    const int64_t base = st_base[wave][st];
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          const int t = ts + 16 * tau + r16;
-          kok[tau] = pok && t < te;
+    for (int tau = 0; tau < 2; ++tau) {
+      const int ti = min(16 * tau + r16, len - 1);
+      // (an absent page reads row 0 instead: results are then unspecified,
+      // but every access stays inside the pool)
+      const int64_t off = whole_page ? base + ti * row_bytes
+                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
 #pragma unroll
-          for (int c = 0; c < KC; ++c)
-            kr[tau][c] = kok[tau] ? *reinterpret_cast<const uint4*>(
-                                        kv.k_pool + base + (16 * tau + r16) * row_bytes +
-                                        (32 * c + 8 * grp) * EB)
-                                  : make_uint4(0, 0, 0, 0);
-        }
+      for (int c = 0; c < KC; ++c)
+        R.k[tau][c] = *reinterpret_cast<const uint4*>(kv.k_pool + off + (32 * c + 8 * grp) * EB);
+    }
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          const int tt = TPV * u + vt;
-          vr[u] = (pok && ts + tt < te)
-                      ? *reinterpret_cast<const uint4*>(kv.v_pool + base + tt * row_bytes + vd * EB)
-                      : make_uint4(0, 0, 0, 0);
-        }
-      } else {
+    for (int u = 0; u < NV; ++u) {
+      const int ti = min(TPV * u + vt, len - 1);
+      const int64_t off = whole_page ? base + ti * row_bytes
+                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+      R.v[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB);
+    }
+  };
+  // Fold stage R (len valid tokens) into the online-softmax state.
+  auto consume = [&](const StageRegs<D>& R, int len) {
+    if (len == 0) return;
+    f32x4_t acc[2];
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          const int t = ts + 16 * tau + r16;
-          const int64_t off = t < te ? row_offset(kv, b, g, t) : -1;
-          kok[tau] = off >= 0;
+    for (int tau = 0; tau < 2; ++tau) {
+      acc[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < KC; ++c)
-            kr[tau][c] = kok[tau] ? *reinterpret_cast<const uint4*>(kv.k_pool + off +
-                                                                    (32 * c + 8 * grp) * EB)
-                                  : make_uint4(0, 0, 0, 0);
-        }
+      for (int c = 0; c < KC; ++c)
+        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            aq[c], __builtin_bit_cast(bf16x8_t, R.k[tau][c]), acc[tau], 0, 0, 0);
+    }
+    // register i of lane (grp, r16) holds head 4 i + grp
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-          const int t = ts + TPV * u + vt;
-          const int64_t off = t < te ? row_offset(kv, b, g, t) : -1;
-          vr[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB)
-                           : make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < GR; ++i) {
+      const float x0 = r16 < len ? acc[0][i] * scale : -INFINITY;
+      const float x1 = 16 + r16 < len ? acc[1][i] * scale : -INFINITY;
+      const float mx = group_max<16>(fmaxf(x0, x1));
+      const float mn = fmaxf(m_run[i], mx);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2f(m_run[i] - ms);
+      const float p0 = exp2f(x0 - ms), p1 = exp2f(x1 - ms);
+      l_run[i] = l_run[i] * alpha + p0 + p1;
+      m_run[i] = mn;
+      const int j = 4 * i + grp;
+      if (j < G) {
+        sp[wave][r16][j] = p0;
+        sp[wave][16 + r16][j] = p1;
+        if (r16 == 0) salpha[wave][j] = alpha;
       }
-      // q.k for the two 16-token tiles
-      f32x4_t acc[2];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // p.v on the VALU: lane (vt, vd) accumulates its tokens into dims vd..vd+7
+    float al[G];
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        acc[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G; ++j) al[j] = salpha[wave][j];
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              aq[c], __builtin_bit_cast(bf16x8_t, kr[tau][c]), acc[tau], 0, 0, 0);
-      }
-      // online softmax; register i of lane (grp, r16) holds head 4 i + grp
+    for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int i = 0; i < GR; ++i) {
-        const float x0 = kok[0] ? acc[0][i] * scale : -INFINITY;
-        const float x1 = kok[1] ? acc[1][i] * scale : -INFINITY;
-        const float mx = group_max<16>(fmaxf(x0, x1));
-        const float mn = fmaxf(m_run[i], mx);
-        const float ms = mn == -INFINITY ? 0.f : mn;
-        const float alpha = exp2f(m_run[i] - ms);
-        const float p0 = exp2f(x0 - ms), p1 = exp2f(x1 - ms);
-        l_run[i] = l_run[i] * alpha + p0 + p1;
-        m_run[i] = mn;
-        const int j = 4 * i + grp;
-        if (j < G) {
-          sp[wave][r16][j] = p0;
-          sp[wave][16 + r16][j] = p1;
-          if (r16 == 0) salpha[wave][j] = alpha;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      // p.v on the VALU: lane (vt, vd) accumulates its tokens into dims vd..vd+7
-      float al[G];
+      for (int k = 0; k < 8; ++k) o[j][k] *= al[j];
 #pragma unroll
-      for (int j = 0; j < G; ++j) al[j] = salpha[wave][j];
+    for (int u = 0; u < NV; ++u) {
+      float vf[8];
+      Vec16<bf16_t>::unpack(R.v[u], vf);
+      const int tt = TPV * u + vt;
+      float pj[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) pj[j] = sp[wave][tt][j];
 #pragma unroll
       for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[j][k] *= al[j];
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        float vf[8];
-        Vec16<bf16_t>::unpack(vr[u], vf);
-        const int tt = TPV * u + vt;
-        float pj[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) pj[j] = sp[wave][tt][j];
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[j][k] = fmaf(pj[j], vf[k], o[j][k]);
-      }
-      __builtin_amdgcn_wave_barrier();
+        for (int k = 0; k < 8; ++k) o[j][k] = fmaf(pj[j], vf[k], o[j][k]);
     }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Stage table: wave w owns entries e0 + w + 4 i; an entry has ceil(S / 32)
+  // stages. One lane per stage looks up the block id and the page and records
+  // the stage's first row (byte offset, or its first token when a stage may
+  // straddle pages) and its number of valid tokens, so that the pipeline
+  // below never waits on a lookup.
+  const int spe = (S + 31) / 32;
+  const int first = e0 + wave;
+  const int nent = first < e1 ? (e1 - first + kDecWaves - 1) / kDecWaves : 0;
+  const int nst = nent * spe;
+  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
+  for (int c0 = 0; c0 < nst; c0 += kStagesPerChunk) {
+    const int cst = min(kStagesPerChunk, nst - c0);
+    if (lane < cst) {
+      const int st = c0 + lane, i = st / spe, sub = st % spe;
+      const int beta = ids[first + kDecWaves * i];
+      int64_t base = 0;
+      int len = 0;
+      if ((unsigned)beta < (unsigned)nb) {
+        const int ts = beta * S + 32 * sub, te = min(beta * S + S, T);
+        len = max(0, min(32, te - ts));
+        if (whole_page && len > 0) {
+          const int page = kv.page_table[(int64_t)b * kv.max_pages + ts / kv.page_size];
+          if ((unsigned)page < (unsigned)kv.num_phys_pages)
+            base = (((int64_t)page * kv.num_kv_heads + g) * kv.page_size + ts % kv.page_size) *
+                   row_bytes;
+          else
+            len = 0;  // absent page: the stage contributes nothing
+        } else {
+          base = ts;
+        }
+      }
+      st_base[wave][lane] = base;
+      st_len[wave][lane] = len;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // two-deep software pipeline: stage s + 1 is loading while s computes
+    StageRegs<D> A, B;
+    int lenA = 0, lenB = 0;
+    issue(0, A, lenA);
+    for (int st = 0; st < cst; st += 2) {
+      if (st + 1 < cst) issue(st + 1, B, lenB);
+      consume(A, lenA);
+      if (st + 1 >= cst) break;
+      if (st + 2 < cst) issue(st + 2, A, lenA);
+      consume(B, lenB);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
   // the running max is uniform per head across the wave, so the token groups'
   // partial sums add without rescaling
@@ -516,11 +552,11 @@ hipError_t launch_f32(const DecodeParams& p, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-// Each of the 4 waves of a workgroup takes one block (several when blocks
-// are short), so a workgroup reads about 4 * max(S, 32) tokens; long id
+// A workgroup takes about 512 tokens (each of its 4 waves a quarter of the
+// blocks), so that every wave pipelines several 32-token stages; long id
 // lists get more blocks per split so that a unit has at most kMaxSplits.
 int decode_blocks_per_split(int block_size, int max_selected) {
-  int bps = block_size >= 32 ? 4 : 4 * ((32 + block_size - 1) / block_size);
+  int bps = block_size >= 128 ? 4 : 4 * ((128 + block_size - 1) / block_size);
   const int need = (max_selected + kMaxSplits - 1) / kMaxSplits;
   if (bps < need) bps = (need + 3) / 4 * 4;
   return bps;
