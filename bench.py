@@ -9,8 +9,10 @@ seeded synthetic data (synth/), resident in HBM before timing starts.
 
 One step = the whole decode-time path through the C ABI:
   1. hs_build_summaries from the last block on (refresh of the growing block),
-  2. hs_select_blocks (score all 4096 blocks per unit, top-k, window union),
-  3. hs_sparse_decode (exact softmax attention over the selected blocks).
+  2. hs_select_decode: selection (score all 4096 blocks per unit, top-k,
+     window union) and exact softmax attention over the selected blocks, in
+     one launch (--path separate: hs_select_blocks then hs_sparse_decode,
+     same results).
 
 The per-step working set (summaries + selected KV, ~143 MB) would fit in the
 256 MiB Infinity Cache, so the timed loop rotates over `--copies` identical
@@ -50,6 +52,7 @@ def parse():
     ap.add_argument("--event-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--path", choices=["fused", "separate"], default="fused")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
                     help="copy: plain device-to-device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -65,11 +68,12 @@ def source_digest(files):
     return h.hexdigest()
 
 
+_CSRC = "hierarchical_sparse_attention_amd/csrc/"
 KERNEL_SOURCES = {
-    "hs_sparse_decode": ["hierarchical_sparse_attention_amd/csrc/decode.hip",
-                         "hierarchical_sparse_attention_amd/csrc/hs_internal.h"],
-    "hs_select_blocks": ["hierarchical_sparse_attention_amd/csrc/select.hip",
-                         "hierarchical_sparse_attention_amd/csrc/hs_internal.h"],
+    "hs_sparse_decode": [_CSRC + f for f in ("decode.hip", "decode_impl.h", "hs_internal.h")],
+    "hs_select_blocks": [_CSRC + f for f in ("select.hip", "select_impl.h", "hs_internal.h")],
+    "hs_select_decode": [_CSRC + f for f in ("step.hip", "select_impl.h", "decode_impl.h",
+                                             "hs_internal.h")],
 }
 
 
@@ -149,8 +153,10 @@ def main():
         ws_s = hs.workspace(hs.hs_select_workspace_size(kv, fine, w.hq, w.top_k, w.window, cap),
                             dev)
         ws_d = hs.workspace(hs.hs_decode_workspace_size(kv, w.hq, w.S, cap), dev)
+        ws_f = hs.workspace(hs.hs_select_decode_workspace_size(kv, fine, w.hq, w.top_k, w.window,
+                                                               cap), dev)
         copies.append(dict(kv=kv, fine=fine, q=q, ids=ids, cnt=cnt, out=out, ws_s=ws_s,
-                           ws_d=ws_d))
+                           ws_d=ws_d, ws_f=ws_f))
     torch.cuda.synchronize()
 
     # full summary build (prefill phase; reported separately, not part of a step)
@@ -167,6 +173,8 @@ def main():
     log("full summary build: %.3f ms, %.0f GB/s" % (build_avg, build_bytes / build_avg / 1e6))
 
     last_block = (w.T - 1) // w.S
+    names = ["hs_build_summaries(last block)", "hs_select_blocks", "hs_sparse_decode",
+             "hs_select_decode"]
     for c in copies:
         c["calls"] = [
             hs.prepare_build_summaries(c["kv"], c["fine"], last_block, stream),
@@ -174,11 +182,14 @@ def main():
                                      c["cnt"], c["ws_s"], stream),
             hs.prepare_sparse_decode(c["kv"], c["q"], w.S, c["ids"], c["cnt"], c["out"],
                                      c["ws_d"], stream),
+            hs.prepare_select_decode(c["kv"], c["q"], c["fine"], w.top_k, w.window, c["ids"],
+                                     c["cnt"], c["out"], c["ws_f"], stream),
         ]
+    step_calls = [0, 3] if args.path == "fused" else [0, 1, 2]
 
     def step(c):
-        for call in c["calls"]:
-            call()
+        for j in step_calls:
+            c["calls"][j]()
 
     # ------------------------------------------------ per-call event timing
     # Each entry point is captured as a graph of back-to-back launches, one per
@@ -190,7 +201,7 @@ def main():
             step(c)
     torch.cuda.synchronize()
     call_ms = []
-    for j in range(3):
+    for j in range(len(names)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for c in copies:
@@ -208,7 +219,8 @@ def main():
         call_ms.append(float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(copies))
         del g
     call_ms = np.array(call_ms)
-    log("per-call mean ms: refresh %.4f select %.4f decode %.4f" % tuple(call_ms))
+    log("per-call mean ms: refresh %.4f select %.4f decode %.4f select+decode %.4f" %
+        tuple(call_ms))
 
     # ---------------------------------------------------------- graphs
     graphs = None
@@ -273,9 +285,13 @@ def main():
 
     dec_ms = float(call_ms[2])
     sel_ms = float(call_ms[1])
-    dominant = "hs_sparse_decode" if bytes_decode >= bytes_select else "hs_select_blocks"
-    dom_bytes, dom_ms = ((bytes_decode, dec_ms) if dominant == "hs_sparse_decode"
-                         else (bytes_select, sel_ms))
+    fused_ms = float(call_ms[3])
+    if args.path == "fused":
+        dominant, dom_bytes, dom_ms = "hs_select_decode", bytes_select + bytes_decode, fused_ms
+    elif bytes_decode >= bytes_select:
+        dominant, dom_bytes, dom_ms = "hs_sparse_decode", bytes_decode, dec_ms
+    else:
+        dominant, dom_bytes, dom_ms = "hs_select_blocks", bytes_select, sel_ms
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     qheads = w.batch * w.hq
 
@@ -300,19 +316,23 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.d, "context": w.T, "summary": w.kind, "block": w.S,
                    "page": w.page_size, "top_k": w.top_k, "window": w.window,
-                   "graph": graphs is not None, "input_copies": len(copies)},
+                   "path": args.path, "graph": graphs is not None,
+                   "input_copies": len(copies)},
         "effective_GBps": bytes_step / (ms_per_step * 1e-3) / 1e9,
         "effective_frac_of_peak": bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "bytes_per_step": bytes_step,
-        "per_call_ms": {"hs_build_summaries(last block)": float(call_ms[0]),
-                        "hs_select_blocks": sel_ms, "hs_sparse_decode": dec_ms},
+        "per_call_ms": {n: float(v) for n, v in zip(names, call_ms)},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dominant, w.name),
                      "bytes_per_launch": dom_bytes, "avg_ms": dom_ms},
-        "select_roofline": {"achieved": bytes_select / (sel_ms * 1e-3) / 1e9,
-                            "bytes_per_launch": bytes_select, "avg_ms": sel_ms,
-                            "traffic": measured_traffic("hs_select_blocks", w.name)},
+        "separate_calls": {
+            "hs_select_blocks": {"GBps": bytes_select / (sel_ms * 1e-3) / 1e9,
+                                 "bytes_per_launch": bytes_select, "avg_ms": sel_ms,
+                                 "traffic": measured_traffic("hs_select_blocks", w.name)},
+            "hs_sparse_decode": {"GBps": bytes_decode / (dec_ms * 1e-3) / 1e9,
+                                 "bytes_per_launch": bytes_decode, "avg_ms": dec_ms,
+                                 "traffic": measured_traffic("hs_sparse_decode", w.name)}},
         "summary_build": {"ms": build_avg, "GBps": build_bytes / build_avg / 1e6},
         "warm_ms_per_step_single_copy": warm_ms,
         "cpu_baseline": cpu,

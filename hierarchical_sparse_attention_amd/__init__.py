@@ -26,7 +26,8 @@ KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 
 # Names declared in include/hs_attn.h; the CPU tests check that each is exported.
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
-           "hs_select_blocks", "hs_sparse_decode", "hs_status_string", "hs_version")
+           "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
+           "hs_select_decode", "hs_status_string", "hs_version")
 
 
 class HsError(RuntimeError):
@@ -76,8 +77,14 @@ def lib() -> ctypes.CDLL:
                                        P(hs_summaries), vp, vp, vp, sz, vp]
         L.hs_sparse_decode.argtypes = [P(hs_kv_cache), vp, i32, ctypes.c_float, i32, vp, vp, i32,
                                        vp, vp, sz, vp]
+        L.hs_select_decode_workspace_size.argtypes = [P(hs_select_params), P(hs_kv_cache),
+                                                      P(hs_summaries), P(hs_summaries), P(sz)]
+        L.hs_select_decode.argtypes = [P(hs_select_params), P(hs_kv_cache), vp,
+                                       P(hs_summaries), P(hs_summaries), ctypes.c_float, vp, vp,
+                                       vp, vp, sz, vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
-                     "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode"):
+                     "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
+                     "hs_select_decode_workspace_size", "hs_select_decode"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -238,6 +245,50 @@ def hs_sparse_decode(kv: KVCache, q: torch.Tensor, block_size: int, block_ids: t
                                   _stream(stream)))
 
 
+def hs_select_decode_workspace_size(kv: KVCache, fine: Summaries, num_q_heads: int, top_k: int,
+                                    window: int, max_selected: int,
+                                    coarse: Optional[Summaries] = None,
+                                    top_k_coarse: int = 0) -> int:
+    p = hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected)
+    n = ctypes.c_size_t(0)
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    _check("hs_select_decode_workspace_size",
+           lib().hs_select_decode_workspace_size(ctypes.byref(p), ctypes.byref(ks),
+                                                 ctypes.byref(fs),
+                                                 ctypes.byref(cs) if cs is not None else None,
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out, workspace,
+                        coarse, top_k_coarse, scale, stream):
+    if block_ids.dtype != torch.int32 or num_selected.dtype != torch.int32:
+        raise ValueError("block_ids and num_selected must be int32")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    args = (ctypes.byref(p), ctypes.byref(ks), _ptr(q), ctypes.byref(fs),
+            ctypes.byref(cs) if cs is not None else None, ctypes.c_float(scale),
+            _ptr(block_ids), _ptr(num_selected), _ptr(out), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    keep = (p, ks, fs, cs, kv, q, fine, coarse, block_ids, num_selected, out, workspace)
+    return args, keep
+
+
+def hs_select_decode(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                     block_ids: torch.Tensor, num_selected: torch.Tensor, out: torch.Tensor,
+                     workspace: torch.Tensor, coarse: Optional[Summaries] = None,
+                     top_k_coarse: int = 0, scale: float = 0.0, stream=None) -> None:
+    """hs_select_blocks then hs_sparse_decode (block size fine.block_size) in
+    one launch; same arguments and outputs as those two calls."""
+    args, _ = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
+                                  workspace, coarse, top_k_coarse, scale, stream)
+    _check("hs_select_decode", lib().hs_select_decode(*args))
+
+
 def hs_version() -> int:
     return lib().hs_version()
 
@@ -293,3 +344,12 @@ def prepare_sparse_decode(kv: KVCache, q: torch.Tensor, block_size: int, block_i
             workspace.numel(), _stream(stream))
     return Prepared("hs_sparse_decode", lib().hs_sparse_decode, args,
                     (ks, kv, q, block_ids, num_selected, out, workspace))
+
+
+def prepare_select_decode(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                          block_ids: torch.Tensor, num_selected: torch.Tensor, out: torch.Tensor,
+                          workspace: torch.Tensor, stream, coarse: Optional[Summaries] = None,
+                          top_k_coarse: int = 0, scale: float = 0.0) -> Prepared:
+    args, keep = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
+                                     workspace, coarse, top_k_coarse, scale, stream)
+    return Prepared("hs_select_decode", lib().hs_select_decode, args, keep)

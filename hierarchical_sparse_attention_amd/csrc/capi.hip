@@ -162,6 +162,110 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
 
 hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
 
+// Workspace of hs_select_decode: [selection workspace][decode workspace]
+// [ready flags, one per unit].
+struct StepLayout {
+  SelectLayout sel;
+  DecodeLayout dec;
+  size_t off_sel, off_dec, off_ready, total;
+};
+
+hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_summaries* fine,
+                     const hs_summaries* coarse, StepLayout* L) {
+  hs_status st = check_select(p, kv, fine, coarse, &L->sel);
+  if (st != HS_OK) return st;
+  st = check_decode(kv, p->num_q_heads, fine->block_size, p->max_selected, &L->dec);
+  if (st != HS_OK) return st;
+  const int64_t chunks = hs::step_chunks((int32_t)L->sel.fine_slots);
+  if (L->sel.units * (chunks + L->dec.max_splits) > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
+  L->off_sel = 0;
+  L->off_dec = align_up(L->sel.total);
+  L->off_ready = align_up(L->off_dec + L->dec.total);
+  L->total = align_up(L->off_ready + sizeof(int32_t) * L->sel.units);
+  return HS_OK;
+}
+
+// Selection parameters of the last level (the only one, or the fine level
+// of two); a two-level selection first launches its coarse level on s.
+hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                        const hs_summaries* fine, const hs_summaries* coarse,
+                        int32_t* block_ids, int32_t* num_selected, uint8_t* ws,
+                        const SelectLayout& L, hipStream_t s, hs::SelectParams* out) {
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+  hs::SelectParams sp;
+  sp.kv = view_of(kv);
+  sp.q = q;
+  sp.G = prm->num_q_heads / kv->num_kv_heads;
+  int32_t* gamma = nullptr;
+  int32_t* gamma_cnt = nullptr;
+  if (L.two_level) {
+    gamma = reinterpret_cast<int32_t*>(ws + L.off_gamma);
+    gamma_cnt = reinterpret_cast<int32_t*>(ws + L.off_gamma_cnt);
+    sp.summ = coarse->data;
+    sp.kind = coarse->kind;
+    sp.block_size = coarse->block_size;
+    sp.max_blocks = coarse->max_blocks;
+    sp.gamma = nullptr;
+    sp.gamma_cnt = nullptr;
+    sp.gamma_cap = 0;
+    sp.ratio = 1;
+    sp.n_slots_max = (int32_t)L.nc;
+    sp.scores = reinterpret_cast<float*>(ws + L.off_coarse_scores);
+    sp.top_k = prm->top_k_coarse;
+    sp.window = 0;
+    sp.out_ids = gamma;
+    sp.out_cnt = gamma_cnt;
+    sp.out_cap = (int32_t)L.kc_cap;
+    sp.out_blocks_max = (int32_t)L.nc;
+    sp.counters = counters + L.units;
+    const hipError_t e = hs::launch_select(sp, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  sp.summ = fine->data;
+  sp.kind = fine->kind;
+  sp.block_size = fine->block_size;
+  sp.max_blocks = fine->max_blocks;
+  sp.gamma = gamma;
+  sp.gamma_cnt = gamma_cnt;
+  sp.gamma_cap = (int32_t)L.kc_cap;
+  sp.ratio = (int32_t)L.ratio;
+  sp.n_slots_max = (int32_t)L.fine_slots;
+  sp.scores = reinterpret_cast<float*>(ws + L.off_fine_scores);
+  sp.top_k = prm->top_k;
+  sp.window = prm->window_tokens;
+  sp.out_ids = block_ids;
+  sp.out_cnt = num_selected;
+  sp.out_cap = prm->max_selected;
+  sp.out_blocks_max = (int32_t)L.nb_fine;
+  sp.counters = counters;
+  *out = sp;
+  return HS_OK;
+}
+
+hs::DecodeParams decode_params(const hs_kv_cache* kv, const void* q, float scale,
+                               int32_t block_size, const int32_t* block_ids,
+                               const int32_t* num_selected, int32_t max_selected, float* out,
+                               uint8_t* ws, const DecodeLayout& L) {
+  if (scale == 0.f) scale = 1.0f / sqrtf((float)kv->head_dim);
+  hs::DecodeParams p;
+  p.kv = view_of(kv);
+  p.q = q;
+  p.G = (int32_t)L.G;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.block_size = block_size;
+  p.ids = block_ids;
+  p.counts = num_selected;
+  p.max_selected = max_selected;
+  p.blocks_per_split = (int32_t)L.bps;
+  p.max_splits = (int32_t)L.max_splits;
+  p.part_o = reinterpret_cast<float*>(ws + L.off_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
+  p.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+  p.ready = nullptr;
+  p.out = out;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,54 +329,10 @@ hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, c
   if (!q || !aligned16(q) || !block_ids || !num_selected) return HS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
   hs::SelectParams sp;
-  sp.kv = view_of(kv);
-  sp.q = q;
-  sp.G = prm->num_q_heads / kv->num_kv_heads;
-  hipError_t e;
-  int32_t* gamma = nullptr;
-  int32_t* gamma_cnt = nullptr;
-  if (L.two_level) {
-    gamma = reinterpret_cast<int32_t*>(ws + L.off_gamma);
-    gamma_cnt = reinterpret_cast<int32_t*>(ws + L.off_gamma_cnt);
-    sp.summ = coarse->data;
-    sp.kind = coarse->kind;
-    sp.block_size = coarse->block_size;
-    sp.max_blocks = coarse->max_blocks;
-    sp.gamma = nullptr;
-    sp.gamma_cnt = nullptr;
-    sp.gamma_cap = 0;
-    sp.ratio = 1;
-    sp.n_slots_max = (int32_t)L.nc;
-    sp.scores = reinterpret_cast<float*>(ws + L.off_coarse_scores);
-    sp.top_k = prm->top_k_coarse;
-    sp.window = 0;
-    sp.out_ids = gamma;
-    sp.out_cnt = gamma_cnt;
-    sp.out_cap = (int32_t)L.kc_cap;
-    sp.out_blocks_max = (int32_t)L.nc;
-    sp.counters = counters + L.units;
-    if ((e = hs::launch_select(sp, s)) != hipSuccess) return from_hip(e);
-  }
-  sp.summ = fine->data;
-  sp.kind = fine->kind;
-  sp.block_size = fine->block_size;
-  sp.max_blocks = fine->max_blocks;
-  sp.gamma = gamma;
-  sp.gamma_cnt = gamma_cnt;
-  sp.gamma_cap = (int32_t)L.kc_cap;
-  sp.ratio = (int32_t)L.ratio;
-  sp.n_slots_max = (int32_t)L.fine_slots;
-  sp.scores = reinterpret_cast<float*>(ws + L.off_fine_scores);
-  sp.top_k = prm->top_k;
-  sp.window = prm->window_tokens;
-  sp.out_ids = block_ids;
-  sp.out_cnt = num_selected;
-  sp.out_cap = prm->max_selected;
-  sp.out_blocks_max = (int32_t)L.nb_fine;
-  sp.counters = counters;
+  st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected,
+                     static_cast<uint8_t*>(workspace), L, s, &sp);
+  if (st != HS_OK) return st;
   return from_hip(hs::launch_select(sp, s));
 }
 
@@ -286,24 +346,47 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q, int32_t num_q_h
   if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
   if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
-  if (scale == 0.f) scale = 1.0f / sqrtf((float)kv->head_dim);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hs::DecodeParams p;
-  p.kv = view_of(kv);
-  p.q = q;
-  p.G = (int32_t)L.G;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.block_size = block_size;
-  p.ids = block_ids;
-  p.counts = num_selected;
-  p.max_selected = max_selected;
-  p.blocks_per_split = (int32_t)L.bps;
-  p.max_splits = (int32_t)L.max_splits;
-  p.part_o = reinterpret_cast<float*>(ws + L.off_o);
-  p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
-  p.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
-  p.out = out;
+  const hs::DecodeParams p = decode_params(kv, q, scale, block_size, block_ids, num_selected,
+                                           max_selected, out, static_cast<uint8_t*>(workspace), L);
   return from_hip(hs::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_select_decode_workspace_size(const hs_select_params* p, const hs_kv_cache* kv,
+                                          const hs_summaries* fine, const hs_summaries* coarse,
+                                          size_t* bytes) {
+  if (!bytes) return HS_ERR_INVALID_ARG;
+  StepLayout L;
+  const hs_status st = check_step(p, kv, fine, coarse, &L);
+  if (st == HS_OK) *bytes = L.total;
+  return st;
+}
+
+hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                           const hs_summaries* fine, const hs_summaries* coarse, float scale,
+                           int32_t* block_ids, int32_t* num_selected, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  StepLayout L;
+  hs_status st = check_step(prm, kv, fine, coarse, &L);
+  if (st != HS_OK) return st;
+  if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hs::StepParams p;
+  st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected, ws + L.off_sel, L.sel, s,
+                     &p.sel);
+  if (st != HS_OK) return st;
+  p.dec = decode_params(kv, q, scale, fine->block_size, block_ids, num_selected,
+                        prm->max_selected, out, ws + L.off_dec, L.dec);
+  p.ready = reinterpret_cast<int32_t*>(ws + L.off_ready);
+  p.dec.ready = p.ready;
+  p.units = (int32_t)L.sel.units;
+  p.n_chunks = hs::step_chunks(p.sel.n_slots_max);
+  p.n_splits = (int32_t)L.dec.max_splits;
+  p.lookahead = p.units;
+  p.total = p.units * (p.n_chunks + p.n_splits);
+  return from_hip(hs::launch_step(p, s));
 }
 
 }  // extern "C"

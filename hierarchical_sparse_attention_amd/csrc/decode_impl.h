@@ -1,0 +1,586 @@
+// decode_impl.h - device code of stage 3, exact softmax attention over the
+// selected blocks read in place from the paged KV cache; shared by the decode
+// kernel and the fused select-and-decode kernel.
+//
+// Sources: "8x256K ... porting HiSparse to QSA" section 3.3 (the attention
+// loop walks a compact list of selected blocks instead of all blocks, with an
+// online softmax) and section 2.3 (no gather of the selected KV into a
+// compact copy); "SparDA" article section 3.3 (only the selected pages are
+// read) and section 3.4 (one block list shared by every layer).
+//
+// Work split: one task per (unit, split). A workgroup of 4 waves owns a run of
+// blocks_per_split consecutive entries of a unit's id list; each wave takes
+// every fourth entry and keeps an fp32 online-softmax state (m, l, o) for
+// the unit's G query heads. The workgroup combines its waves in LDS, writes
+// one partial per split, and the last workgroup of the unit to finish
+// (arrival counter in the workspace) merges the unit's partials into the
+// output with the log-sum-exp rule, so one launch does the whole stage.
+//
+// k_decode_bf16 (bf16 caches): q.k on the matrix cores. For a 16-token tile
+// v_mfma_f32_16x16x32_bf16 takes the unit's query heads as rows of A (head j
+// in row 4 (j % 4) + j / 4, so every 16-lane group of the result holds one
+// head's 16 logits) and the K tile as B: each lane's 16-byte load of
+// 8 consecutive dims of one token is exactly its B operand, so K goes from
+// HBM to the MFMA without any shuffle. Softmax statistics are per head and
+// wave-uniform; p and the rescale factor go through a small per-wave LDS
+// slice to the p.v accumulation, which runs on the VALU in fp32 with V read
+// as 16-byte rows (lane: 8 dims of one token).
+// k_decode_f32 (float32 caches): all on the VALU; the q.k dot is reduced
+// across the lanes of a token row with DPP.
+// Logits are kept in base 2: the logit scale is multiplied by log2(e), so
+// exp(l - m) = exp2(l2 - m2) in real arithmetic.
+#pragma once
+
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+constexpr int kDecWaves = 4;
+// The host keeps the number of splits of a unit at most kMaxSplits (it grows
+// blocks_per_split for very long id lists), so the merge's (m, l) table of
+// 2 * kMaxSplits * G floats fits in the 4 * G * D floats of the wave area.
+constexpr int kMaxSplits = 128;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int D, int G>
+struct SplitShared {
+  float o[kDecWaves][G][D];
+  float m[kDecWaves][G];
+  float l[kDecWaves][G];
+  int last;
+};
+
+__device__ __forceinline__ int clamp_count(const DecodeParams& p, int unit) {
+  int cnt = published_i32(&p.counts[unit]);
+  return cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void merge_unit(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns);
+
+// An empty selection has no split to merge: its output rows are zero.
+template <int D, int G>
+__device__ __forceinline__ void write_empty(const DecodeParams& p, int unit) {
+  const int Hq = p.kv.num_kv_heads * G;
+  const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
+  for (int idx = thread_id(); idx < G * D; idx += blockDim.x)
+    p.out[((int64_t)b * Hq + g * G) * D + idx] = 0.f;
+}
+
+// Arrival of one split task of the unit (of `expected`). The last one clears
+// the unit's ready flag (fused launch: every task of the unit has read it by
+// then) and merges the unit's ns partials.
+template <int D, int G>
+__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns,
+                                 int expected) {
+  if (!arrive_last(&p.counters[unit], expected, &sh.last)) return;
+  if (p.ready != nullptr && thread_id() == 0) publish_i32(&p.ready[unit], 0);
+  if (ns == 0) write_empty<D, G>(p, unit);
+  else merge_unit<D, G>(p, sh, unit, ns);
+}
+
+// Combine the waves of this workgroup, publish the split's partial and arrive.
+template <int D, int G>
+__device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int split,
+                             int ns, int expected) {
+  const int tid = thread_id();
+  __syncthreads();
+  const int64_t ps = (int64_t)unit * p.max_splits + split;
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    const int j = idx / D, dd = idx % D;
+    float mn = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mn = fmaxf(mn, sh.m[w][j]);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float a = exp2f(sh.m[w][j] - ms);
+      acc += sh.o[w][j][dd] * a;
+      lsum += sh.l[w][j] * a;
+    }
+    publish(&p.part_o[(ps * G + j) * D + dd], acc);
+    if (dd == 0) {
+      publish(&p.part_ml[(ps * G + j) * 2 + 0], mn);
+      publish(&p.part_ml[(ps * G + j) * 2 + 1], lsum);
+    }
+  }
+  arrive_and_merge<D, G>(p, sh, unit, ns, expected);
+}
+
+// Log-sum-exp merge of a unit's ns <= kMaxSplits split partials into `out`,
+// by the unit's last-arriving workgroup. Thread t < stride owns output
+// elements t + r * stride of the unit's G x D block (r < R). The (m, l) loads
+// and the first kMergeBatch partial-output loads are issued together, so for
+// the usual split counts the whole merge costs one round trip to the
+// device-coherent level.
+template <int D, int G>
+__device__ __forceinline__ void merge_unit(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns) {
+  const int tid = thread_id();
+  constexpr int stride = G * D < 256 ? G * D : 256;
+  constexpr int R = G * D / stride;
+  constexpr int kMergeBatch = 80;
+  float* sm = &sh.o[0][0][0];                 // [ns][G] maxima, then weights
+  float* sl = sm + kMaxSplits * G;            // [ns][G] sums
+  const int64_t p0 = (int64_t)unit * p.max_splits;
+  const int npairs = ns * R;                  // (split, r) loads of this thread
+  const bool owner = tid < stride;
+  float mv = 0.f, lv = 0.f;
+  const bool ml_loader = tid < ns * G;
+  if (ml_loader) {
+    mv = published(&p.part_ml[(p0 * G + tid) * 2]);
+    lv = published(&p.part_ml[(p0 * G + tid) * 2 + 1]);
+  }
+  float v[kMergeBatch];
+#pragma unroll
+  for (int q = 0; q < kMergeBatch; ++q) {
+    const int qq = min(q, npairs - 1);  // unconditional (clamped) loads overlap
+    v[q] = published(&p.part_o[(p0 + qq / R) * G * D + (owner ? tid : 0) + (qq % R) * stride]);
+  }
+  for (int t = tid; t < ns * G; t += blockDim.x) {  // more than 256 (m, l) pairs
+    sm[t] = t == tid ? mv : published(&p.part_ml[(p0 * G + t) * 2]);
+    sl[t] = t == tid ? lv : published(&p.part_ml[(p0 * G + t) * 2 + 1]);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mn = -INFINITY;
+    for (int s = 0; s < ns; ++s) mn = fmaxf(mn, sm[s * G + tid]);
+    sh.m[0][tid] = mn == -INFINITY ? 0.f : mn;
+  }
+  __syncthreads();
+  for (int t = tid; t < ns * G; t += blockDim.x) sm[t] = exp2f(sm[t] - sh.m[0][t % G]);
+  __syncthreads();
+  if (tid < G) {
+    float lsum = 0.f;
+    for (int s = 0; s < ns; ++s) lsum += sl[s * G + tid] * sm[s * G + tid];
+    sh.l[0][tid] = lsum;
+  }
+  __syncthreads();
+  if (!owner) return;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMergeBatch; ++q)
+    if (q < npairs) acc[q % R] += v[q] * sm[(q / R) * G + (tid + (q % R) * stride) / D];
+  for (int q = kMergeBatch; q < npairs; ++q)  // long id lists only
+    acc[q % R] += published(&p.part_o[(p0 + q / R) * G * D + tid + (q % R) * stride]) *
+                  sm[(q / R) * G + (tid + (q % R) * stride) / D];
+  const int Hq = p.kv.num_kv_heads * G;
+  const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = tid + r * stride, j = idx / D;
+    const float lsum = sh.l[0][j];
+    p.out[((int64_t)b * Hq + g * G) * D + idx] = lsum > 0.f ? acc[r] / lsum : 0.f;
+  }
+}
+
+// Entries [e0, e1) of the unit's id list that split task `split` owns, and
+// the unit's split count ns. A task with no entry returns false: in a
+// separate launch (expected == 0, ns arrivals) it only writes the zero output
+// of an empty selection; in a fused launch every task arrives (expected of
+// them), so the last one still merges.
+struct SplitSpan {
+  int ns, e0, e1;
+};
+
+template <int D, int G>
+__device__ __forceinline__ bool split_span(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int split,
+                           int expected, SplitSpan& sp) {
+  const int cnt = clamp_count(p, unit);
+  const int bps = p.blocks_per_split;
+  sp.ns = (cnt + bps - 1) / bps;
+  sp.e0 = split * bps;
+  sp.e1 = min(sp.e0 + bps, cnt);
+  if (sp.e0 < cnt) return true;
+  if (expected == 0) {
+    if (cnt == 0 && split == 0) write_empty<D, G>(p, unit);
+  } else {
+    arrive_and_merge<D, G>(p, sh, unit, sp.ns, expected);
+  }
+  return false;
+}
+
+// --------------------------------------------------------------- bf16 path
+// One 32-token stage of K and V as loaded (two 16-token MFMA tiles of K in
+// B-operand layout, V as 16-byte rows).
+template <int D>
+struct StageRegs {
+  uint4 k[2][D / 32];
+  uint4 v[32 / (kWave / (D / 8))];
+};
+
+constexpr int kStagesPerChunk = kWave;  // stage-table entries filled per pass
+
+// LDS of one split task (both paths; the float32 path uses `sh` only).
+template <int D, int G>
+struct DecodeShared {
+  SplitShared<D, G> sh;
+  float sp[kDecWaves][32][G];
+  float salpha[kDecWaves][G];
+  int64_t st_base[kDecWaves][kStagesPerChunk];  // see the stage table below
+  int st_len[kDecWaves][kStagesPerChunk];
+};
+
+// One split task of a bf16 cache; expected: see split_span.
+template <int D, int G>
+__device__ __forceinline__ void decode_task_bf16(const DecodeParams& p, int unit, int split, int expected,
+                                 DecodeShared<D, G>& ds) {
+  constexpr int KC = D / 32;       // MFMA k-chunks per token row
+  constexpr int VL = D / 8;        // lanes per V row (16 bytes each)
+  constexpr int TPV = kWave / VL;  // tokens per V load instruction
+  constexpr int NV = 32 / TPV;     // V loads per 32-token stage
+  constexpr int GR = (G + 3) / 4;  // MFMA result registers that carry heads
+  constexpr int EB = 2;            // bytes per element
+  SplitShared<D, G>& sh = ds.sh;
+  auto& sp = ds.sp;
+  auto& salpha = ds.salpha;
+  auto& st_base = ds.st_base;
+  auto& st_len = ds.st_len;
+
+  const KvView& kv = p.kv;
+  SplitSpan span;
+  if (!split_span<D, G>(p, sh, unit, split, expected, span)) return;
+  const int e0 = span.e0, e1 = span.e1, ns = span.ns;
+  const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
+  const int T = clamp_len(kv, b);
+  const int S = p.block_size;
+  const int nb = (T + S - 1) / S;
+  const int tid = thread_id();
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int vt = lane / VL, vd = (lane % VL) * 8;
+  const int Hq = kv.num_kv_heads * G;
+  const float scale = p.scale_log2;
+  // a 32-token stage stays inside one page when the page and block sizes are
+  // multiples of 32: then one page lookup serves the whole stage
+  const bool whole_page = (kv.page_size % 32 == 0) && (S % 32 == 0);
+  const int64_t row_bytes = (int64_t)D * EB;
+
+  // A operands: query head j in row 4 (j % 4) + j / 4 (zero rows elsewhere)
+  bf16x8_t aq[KC];
+  {
+    const int j = 4 * (r16 & 3) + (r16 >> 2);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) +
+                          ((int64_t)b * Hq + g * G + (j < G ? j : 0)) * row_bytes;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      uint4 r = j < G ? *reinterpret_cast<const uint4*>(qrow + (32 * c + 8 * grp) * EB)
+                      : make_uint4(0, 0, 0, 0);
+      aq[c] = __builtin_bit_cast(bf16x8_t, r);
+    }
+  }
+  float m_run[GR], l_run[GR], o[G][8];
+#pragma unroll
+  for (int i = 0; i < GR; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[j][k] = 0.f;
+
+  // Issue the loads of stage `st` of the table. Lanes of masked tokens load a
+  // valid row of the same stage instead (their logits are -inf, so their p is
+  // 0 and the finite V row adds nothing); an empty stage loads nothing.
+  auto issue = [&](int st, StageRegs<D>& R, int& len) {
+    len = st_len[wave][st];
+    if (len == 0) return;
+    const int64_t base = st_base[wave][st];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int ti = min(16 * tau + r16, len - 1);
+      // (an absent page reads row 0 instead: results are then unspecified,
+      // but every access stays inside the pool)
+      const int64_t off = whole_page ? base + ti * row_bytes
+                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        R.k[tau][c] = *reinterpret_cast<const uint4*>(kv.k_pool + off + (32 * c + 8 * grp) * EB);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int ti = min(TPV * u + vt, len - 1);
+      const int64_t off = whole_page ? base + ti * row_bytes
+                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+      R.v[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB);
+    }
+  };
+  // Fold stage R (len valid tokens) into the online-softmax state.
+  auto consume = [&](const StageRegs<D>& R, int len) {
+    if (len == 0) return;
+    f32x4_t acc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      acc[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            aq[c], __builtin_bit_cast(bf16x8_t, R.k[tau][c]), acc[tau], 0, 0, 0);
+    }
+    // register i of lane (grp, r16) holds head 4 i + grp
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      const float x0 = r16 < len ? acc[0][i] * scale : -INFINITY;
+      const float x1 = 16 + r16 < len ? acc[1][i] * scale : -INFINITY;
+      const float mx = group_max<16>(fmaxf(x0, x1));
+      const float mn = fmaxf(m_run[i], mx);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2f(m_run[i] - ms);
+      const float p0 = exp2f(x0 - ms), p1 = exp2f(x1 - ms);
+      l_run[i] = l_run[i] * alpha + p0 + p1;
+      m_run[i] = mn;
+      const int j = 4 * i + grp;
+      if (j < G) {
+        sp[wave][r16][j] = p0;
+        sp[wave][16 + r16][j] = p1;
+        if (r16 == 0) salpha[wave][j] = alpha;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // p.v on the VALU: lane (vt, vd) accumulates its tokens into dims vd..vd+7
+    float al[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) al[j] = salpha[wave][j];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[j][k] *= al[j];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float vf[8];
+      Vec16<bf16_t>::unpack(R.v[u], vf);
+      const int tt = TPV * u + vt;
+      float pj[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) pj[j] = sp[wave][tt][j];
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[j][k] = fmaf(pj[j], vf[k], o[j][k]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Stage table: wave w owns entries e0 + w + 4 i; an entry has ceil(S / 32)
+  // stages. One lane per stage looks up the block id and the page and records
+  // the stage's first row (byte offset, or its first token when a stage may
+  // straddle pages) and its number of valid tokens, so that the pipeline
+  // below never waits on a lookup.
+  const int spe = (S + 31) / 32;
+  const int first = e0 + wave;
+  const int nent = first < e1 ? (e1 - first + kDecWaves - 1) / kDecWaves : 0;
+  const int nst = nent * spe;
+  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
+  for (int c0 = 0; c0 < nst; c0 += kStagesPerChunk) {
+    const int cst = min(kStagesPerChunk, nst - c0);
+    if (lane < cst) {
+      const int st = c0 + lane, i = st / spe, sub = st % spe;
+      const int beta = published_i32(&ids[first + kDecWaves * i]);
+      int64_t base = 0;
+      int len = 0;
+      if ((unsigned)beta < (unsigned)nb) {
+        const int ts = beta * S + 32 * sub, te = min(beta * S + S, T);
+        len = max(0, min(32, te - ts));
+        if (whole_page && len > 0) {
+          const int page = kv.page_table[(int64_t)b * kv.max_pages + ts / kv.page_size];
+          if ((unsigned)page < (unsigned)kv.num_phys_pages)
+            base = (((int64_t)page * kv.num_kv_heads + g) * kv.page_size + ts % kv.page_size) *
+                   row_bytes;
+          else
+            len = 0;  // absent page: the stage contributes nothing
+        } else {
+          base = ts;
+        }
+      }
+      st_base[wave][lane] = base;
+      st_len[wave][lane] = len;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // two-deep software pipeline: stage s + 1 is loading while s computes
+    StageRegs<D> A, B;
+    int lenA = 0, lenB = 0;
+    issue(0, A, lenA);
+    for (int st = 0; st < cst; st += 2) {
+      if (st + 1 < cst) issue(st + 1, B, lenB);
+      consume(A, lenA);
+      if (st + 1 >= cst) break;
+      if (st + 2 < cst) issue(st + 2, A, lenA);
+      consume(B, lenB);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // the running max is uniform per head across the wave, so the token groups'
+  // partial sums add without rescaling
+#pragma unroll
+  for (int s = VL; s < kWave; s *= 2)
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[j][k] += __shfl_xor(o[j][k], s);
+#pragma unroll
+  for (int i = 0; i < GR; ++i) l_run[i] = group_sum<16>(l_run[i]);
+  if (lane < VL) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sh.o[wave][j][vd + k] = o[j][k];
+  }
+  if (r16 == 0) {
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      const int j = 4 * i + grp;
+      if (j < G) {
+        sh.m[wave][j] = m_run[i];
+        sh.l[wave][j] = l_run[i];
+      }
+    }
+  }
+  finish_split<D, G>(p, sh, unit, split, ns, expected ? expected : ns);
+}
+
+// -------------------------------------------------------------- float32 path
+// One split task of a float32 cache; expected: see split_span.
+template <int D, int G, int UNR>
+__device__ __forceinline__ void decode_task_f32(const DecodeParams& p, int unit, int split, int expected,
+                                DecodeShared<D, G>& ds) {
+  constexpr int EPL = 4;              // floats per 16-byte load
+  constexpr int LPT = D / EPL;        // lanes per token row
+  constexpr int TPW = kWave / LPT;    // tokens per wave instruction
+  SplitShared<D, G>& sh = ds.sh;
+  const KvView& kv = p.kv;
+  SplitSpan span;
+  if (!split_span<D, G>(p, sh, unit, split, expected, span)) return;
+  const int e0 = span.e0, e1 = span.e1, ns = span.ns;
+  const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
+  const int T = clamp_len(kv, b);
+  const int S = p.block_size;
+  const int nb = (T + S - 1) / S;
+  const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tg = lane / LPT, li = lane % LPT;
+  const int Hq = kv.num_kv_heads * G;
+
+  float qv[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float4 r = *reinterpret_cast<const float4*>(
+        reinterpret_cast<const float*>(p.q) + ((int64_t)b * Hq + g * G + j) * D + li * EPL);
+    qv[j][0] = r.x * p.scale_log2;
+    qv[j][1] = r.y * p.scale_log2;
+    qv[j][2] = r.z * p.scale_log2;
+    qv[j][3] = r.w * p.scale_log2;
+  }
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) o[j][k] = 0.f;
+  }
+  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
+  for (int e = e0 + wave; e < e1; e += kDecWaves) {
+    const int beta = published_i32(&ids[e]);
+    if ((unsigned)beta >= (unsigned)nb) continue;  // wave-uniform
+    const int tb = beta * S, te = min(tb + S, T);
+    for (int t0 = tb; t0 < te; t0 += TPW * UNR) {  // wave-uniform trip count
+      uint4 kr[UNR], vr[UNR];
+      bool ok[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int t = t0 + u * TPW + tg;
+        const int64_t off = t < te ? row_offset(kv, b, g, t) : -1;
+        ok[u] = off >= 0;
+        kr[u] = ok[u] ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
+                      : make_uint4(0, 0, 0, 0);
+        vr[u] = ok[u] ? *reinterpret_cast<const uint4*>(kv.v_pool + off + li * 16)
+                      : make_uint4(0, 0, 0, 0);
+      }
+      float x[UNR][G];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        float kf[EPL];
+        Vec16<float>::unpack(kr[u], kf);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float a = 0.f;
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) a = fmaf(qv[j][k], kf[k], a);
+          a = group_sum<LPT>(a);
+          x[u][j] = ok[u] ? a : -INFINITY;
+        }
+      }
+      float pr[UNR][G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float mx = x[0][j];
+#pragma unroll
+        for (int u = 1; u < UNR; ++u) mx = fmaxf(mx, x[u][j]);
+        const float mn = fmaxf(m[j], mx);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(m[j] - ms);
+        m[j] = mn;
+        l[j] *= alpha;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) o[j][k] *= alpha;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          pr[u][j] = exp2f(x[u][j] - ms);
+          l[j] += pr[u][j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        float vf[EPL];
+        Vec16<float>::unpack(vr[u], vf);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) o[j][k] = fmaf(pr[u][j], vf[k], o[j][k]);
+      }
+    }
+  }
+  // merge the token groups of the wave (their running maxima differ)
+#pragma unroll
+  for (int s = LPT; s < kWave; s *= 2) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float m2 = __shfl_xor(m[j], s);
+      const float l2 = __shfl_xor(l[j], s);
+      const float mn = fmaxf(m[j], m2);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float a1 = exp2f(m[j] - ms), a2 = exp2f(m2 - ms);
+      m[j] = mn;
+      l[j] = l[j] * a1 + l2 * a2;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        const float o2 = __shfl_xor(o[j][k], s);
+        o[j][k] = o[j][k] * a1 + o2 * a2;
+      }
+    }
+  }
+  if (tg == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) sh.o[wave][j][li * EPL + k] = o[j][k];
+      if (li == 0) {
+        sh.m[wave][j] = m[j];
+        sh.l[wave][j] = l[j];
+      }
+    }
+  }
+  finish_split<D, G>(p, sh, unit, split, ns, expected ? expected : ns);
+}
+
+// Unroll of the float32 path's token loop (registers bound it at G = 8).
+template <int G>
+constexpr int f32_unroll() { return G == 8 ? 4 : 8; }
+
+}  // namespace
+}  // namespace hs

@@ -11,6 +11,17 @@ namespace hs {
 
 constexpr int kWave = 64;
 
+// Thread index in the workgroup, read through an empty asm: every call is a
+// new value to the compiler. Task bodies take it once at their start, so in
+// a persistent task loop the per-thread address arithmetic of a task is
+// recomputed per task instead of being hoisted out of the loop, where it
+// would hold registers for the whole kernel.
+__device__ __forceinline__ int thread_id() {
+  int x = threadIdx.x;
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // ----------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -107,12 +118,18 @@ __device__ __forceinline__ void publish(float* p, float v) {
 __device__ __forceinline__ float published(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void publish_i32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t published_i32(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Every thread calls this; returns true in every thread of the workgroup that
 // arrived last (of `expected`) on `counter`, which it then resets to zero.
 __device__ __forceinline__ bool arrive_last(int32_t* counter, int expected, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's published stores are done
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (thread_id() == 0) {
     const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = old == expected - 1;
     if (*flag) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -191,10 +208,21 @@ struct DecodeParams {
   float* part_o;             // [units][max_splits][G][d]
   float* part_ml;            // [units][max_splits][G][2]
   int32_t* counters;         // [units] split arrivals; zero between calls
+  int32_t* ready;            // fused launch: [units] selection-done flags, else null
   float* out;                // [B][Hq][d]
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 int decode_blocks_per_split(int block_size, int max_selected);
+
+// Fused last selection level + decode of one layer (one persistent launch).
+struct StepParams {
+  SelectParams sel;          // the last (or only) selection level
+  DecodeParams dec;          // ids / counts = sel.out_ids / sel.out_cnt
+  int32_t* ready;            // [units] selection-done flags; zero between calls
+  int32_t units, n_chunks, n_splits, lookahead, total;
+};
+hipError_t launch_step(const StepParams& p, hipStream_t s);
+int step_chunks(int32_t n_slots_max);  // scoring tasks per unit
 
 constexpr int kMaxBlocks = 32768;  // blocks per unit of a summary level (LDS bitmap)
 

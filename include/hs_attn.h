@@ -13,6 +13,9 @@
  *   hs_sparse_decode    exact softmax attention over the selected blocks only,
  *                       read in place from a paged KV cache
  *
+ * hs_select_decode runs the last two stages for one layer in a single launch
+ * (same results as hs_select_blocks followed by hs_sparse_decode).
+ *
  * Sources (web pages; cited by title and section):
  *   [QSA]     "8x256K long-context sparse attention: porting HiSparse to QSA"
  *             (xxmr.cn), sections 2.2 (three-level coarse/fine/window
@@ -229,6 +232,34 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
                            int32_t num_q_heads, float scale,
                            int32_t block_size, const int32_t* block_ids,
                            const int32_t* num_selected, int32_t max_selected,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Stages 2 and 3 of one layer in one launch: the selection of
+ * hs_select_blocks and the attention of hs_sparse_decode over the ids it
+ * selects ([QSA 3.2] selection on the GPU, then [QSA 3.3] the attention loop
+ * over the compact index list; [SGL 2.2] decode phase, steps a and b).
+ * Arguments mean what they mean for those two calls; the decode uses
+ * fine->block_size and p->max_selected. block_ids and num_selected are
+ * written as by hs_select_blocks, out as by hs_sparse_decode, and the results
+ * are bitwise identical to the two calls on the same inputs. A two-level
+ * selection launches its coarse level first, then one fused launch.
+ * Inside the launch, a unit's attention starts as soon as that unit's
+ * selection is done, while other units are still being scored.
+ * workspace: device buffer of at least hs_select_decode_workspace_size()
+ *   bytes, 16-byte aligned and ZERO-FILLED before its first use; it holds
+ *   the workspaces of both stages plus per-unit ready flags. Every call returns counters and flags to zero, so it can be
+ *   reused by later calls on the same stream but must not be shared by calls
+ *   that may run at the same time. */
+hs_status hs_select_decode_workspace_size(const hs_select_params* p,
+                                          const hs_kv_cache* kv,
+                                          const hs_summaries* fine,
+                                          const hs_summaries* coarse,
+                                          size_t* bytes);
+hs_status hs_select_decode(const hs_select_params* p, const hs_kv_cache* kv,
+                           const void* q, const hs_summaries* fine,
+                           const hs_summaries* coarse, float scale,
+                           int32_t* block_ids, int32_t* num_selected,
                            float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 

@@ -87,6 +87,25 @@ class Problem:
         hs.hs_select_blocks(kv, q, summ["fine"], k, W, ids, cnt, ws, coarse, w.top_k_coarse)
         return ids, cnt
 
+    def select_decode(self, q: torch.Tensor, summ: Dict[str, hs.Summaries], top_k=None,
+                      window=None, max_selected=None, layer=0, ws=None):
+        """hs_select_decode (one launch); returns ids, counts, out and the
+        workspace (so that a test can call again with the same one)."""
+        w, kv = self.w, self.kvs[layer]
+        k = w.top_k if top_k is None else top_k
+        W = w.window if window is None else window
+        cap = max_selected or min(w.nb, min(k, w.nb) + -(-W // w.S) + 1)
+        ids = torch.full((w.batch, w.hkv, cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+        coarse = summ.get("coarse")
+        if ws is None:
+            n = hs.hs_select_decode_workspace_size(kv, summ["fine"], w.hq, k, W, cap, coarse,
+                                                   w.top_k_coarse)
+            ws = hs.workspace(n, "cuda")
+        hs.hs_select_decode(kv, q, summ["fine"], k, W, ids, cnt, out, ws, coarse, w.top_k_coarse)
+        return ids, cnt, out, ws
+
     def decode(self, q: torch.Tensor, ids: torch.Tensor, cnt: torch.Tensor, layer=0,
                block_size=None):
         w, kv = self.w, self.kvs[layer]

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import hierarchical_sparse_attention_amd as hs
 import oracle
 from gpu_helpers import (Problem, check_ids, check_rows, log, magnitudes, oracle_select,
                          unit_inputs)
@@ -142,6 +143,31 @@ def test_select_and_pipeline_match_oracle(name):
     log("%s pipeline: %d tolerated near-tie differences, max row rel err %.3g" % (name, ties, err))
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_select_decode_equals_separate_calls(name):
+    """hs_select_decode (selection and attention in one launch) gives the
+    same ids, counts and bitwise the same outputs as hs_select_blocks followed
+    by hs_sparse_decode; a second and a third call on the same workspace (its
+    ready flags and arrival counters back at zero) repeat
+    them exactly."""
+    P = problem(name)
+    q = P.q()
+    summ = P.summaries()
+    ids_s, cnt_s = P.select(q, summ)
+    out_s = P.decode(q, ids_s, cnt_s)
+    ws = None
+    for call in range(3):
+        ids_f, cnt_f, out_f, ws = P.select_decode(q, summ, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(cnt_f, cnt_s), (name, call)
+        assert torch.equal(ids_f, ids_s), (name, call)
+        assert torch.equal(out_f, out_s), (name, call, float((out_f - out_s).abs().max()))
+    # the workspace starts with the selection's arrival counters (two levels)
+    units_n = P.w.batch * P.w.hkv
+    assert int(ws[:8 * units_n].view(torch.int32).abs().sum()) == 0, name
+    log("%s fused == separate, 3 calls" % name)
+
+
 @pytest.mark.parametrize("top_k,window", [(0, 256), (0, 0), (10 ** 6, 0), (3, 10 ** 6), (64, 1)])
 def test_selection_edge_values(top_k, window):
     """k = 0 (window only), nothing selected at all, k >= number of blocks
@@ -167,6 +193,10 @@ def test_selection_edge_values(top_k, window):
     check_rows(w, out, ref, "edge k=%d W=%d" % (top_k, window))
     if top_k == 0 and window == 0:
         assert np.all(cnt == 0) and np.all(out == 0)
+    ids_f, cnt_f, out_f, _ = P.select_decode(q, summ, top_k=top_k, window=window,
+                                             max_selected=cap)
+    assert torch.equal(cnt_f, cnt_t) and torch.equal(ids_f, ids_t)
+    assert torch.equal(out_f.cpu().double(), torch.from_numpy(out))
 
 
 def test_page_permutation_invariance_and_determinism():
