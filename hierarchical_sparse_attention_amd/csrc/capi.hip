@@ -81,7 +81,8 @@ int group_size(const hs_kv_cache* kv, int32_t num_q_heads, hs_status* st) {
 struct SelectLayout {
   bool two_level;
   int64_t units, nb_fine, nc, kc_cap, ratio, fine_slots;
-  size_t off_cnt, off_coarse_scores, off_gamma, off_gamma_cnt, off_fine_scores, total;
+  size_t off_cnt, off_coarse_scores, off_coarse_keys, off_gamma, off_gamma_cnt, off_fine_scores,
+      off_fine_keys, total;
 };
 
 hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
@@ -110,8 +111,8 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
   L->two_level = two;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->nb_fine = nb > 0 ? nb : 1;
-  L->off_cnt = 0;
-  size_t off = align_up(sizeof(int32_t) * 2 * L->units);
+  L->off_cnt = 0;  // fine level's counters, then the coarse level's
+  size_t off = align_up(sizeof(int32_t) * hs::kCounterStride * 2 * L->units);
   if (two) {
     L->nc = std::max<int64_t>(1, blocks_needed(kv, coarse->block_size));
     L->kc_cap = std::min<int64_t>(p->top_k_coarse, L->nc);
@@ -119,6 +120,8 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
     L->fine_slots = std::max<int64_t>(1, L->kc_cap * L->ratio);
     L->off_coarse_scores = off;
     off = align_up(off + sizeof(float) * L->units * L->nc);
+    L->off_coarse_keys = off;
+    off = align_up(off + sizeof(uint32_t) * 2 * L->units * hs::step_chunks((int32_t)L->nc));
     L->off_gamma = off;
     off = align_up(off + sizeof(int32_t) * L->units * L->kc_cap);
     L->off_gamma_cnt = off;
@@ -127,17 +130,19 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
     L->nc = L->kc_cap = 0;
     L->ratio = 1;
     L->fine_slots = L->nb_fine;
-    L->off_coarse_scores = L->off_gamma = L->off_gamma_cnt = 0;
+    L->off_coarse_scores = L->off_coarse_keys = L->off_gamma = L->off_gamma_cnt = 0;
   }
   L->off_fine_scores = off;
   off = align_up(off + sizeof(float) * L->units * L->fine_slots);
+  L->off_fine_keys = off;
+  off = align_up(off + sizeof(uint32_t) * 2 * L->units * hs::step_chunks((int32_t)L->fine_slots));
   L->total = off;
   return HS_OK;
 }
 
 // Workspace of hs_sparse_decode: [arrival counters][split partials o][(m, l)].
 struct DecodeLayout {
-  int64_t units, bps, max_splits, G;
+  int64_t units, n_splits, G;
   size_t off_cnt, off_o, off_ml, total;
 };
 
@@ -150,24 +155,21 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
   if (block_size < 1 || max_selected < 1) return HS_ERR_INVALID_ARG;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->G = G;
-  L->bps = hs::decode_blocks_per_split(block_size, max_selected);
-  L->max_splits = ceil_div(max_selected, L->bps);
-  if (L->max_splits > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
+  L->n_splits = hs::decode_splits(L->units, max_selected);
   L->off_cnt = 0;
-  L->off_o = align_up(sizeof(int32_t) * L->units);
-  L->off_ml = align_up(L->off_o + sizeof(float) * L->units * L->max_splits * G * kv->head_dim);
-  L->total = align_up(L->off_ml + sizeof(float) * L->units * L->max_splits * G * 2);
+  L->off_o = align_up(sizeof(int32_t) * hs::kCounterStride * L->units);
+  L->off_ml = align_up(L->off_o + sizeof(float) * L->units * L->n_splits * G * kv->head_dim);
+  L->total = align_up(L->off_ml + sizeof(float) * L->units * L->n_splits * G * 2);
   return HS_OK;
 }
 
 hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
 
-// Workspace of hs_select_decode: [selection workspace][decode workspace]
-// [ready flags, one per unit].
+// Workspace of hs_select_decode: [selection workspace][decode workspace].
 struct StepLayout {
   SelectLayout sel;
   DecodeLayout dec;
-  size_t off_sel, off_dec, off_ready, total;
+  size_t off_sel, off_dec, total;
 };
 
 hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_summaries* fine,
@@ -177,11 +179,10 @@ hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_
   st = check_decode(kv, p->num_q_heads, fine->block_size, p->max_selected, &L->dec);
   if (st != HS_OK) return st;
   const int64_t chunks = hs::step_chunks((int32_t)L->sel.fine_slots);
-  if (L->sel.units * (chunks + L->dec.max_splits) > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
+  if (L->sel.units * (chunks + L->dec.n_splits) > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
   L->off_sel = 0;
   L->off_dec = align_up(L->sel.total);
-  L->off_ready = align_up(L->off_dec + L->dec.total);
-  L->total = align_up(L->off_ready + sizeof(int32_t) * L->sel.units);
+  L->total = align_up(L->off_dec + L->dec.total);
   return HS_OK;
 }
 
@@ -211,13 +212,14 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
     sp.ratio = 1;
     sp.n_slots_max = (int32_t)L.nc;
     sp.scores = reinterpret_cast<float*>(ws + L.off_coarse_scores);
+    sp.chunk_keys = reinterpret_cast<uint32_t*>(ws + L.off_coarse_keys);
     sp.top_k = prm->top_k_coarse;
     sp.window = 0;
     sp.out_ids = gamma;
     sp.out_cnt = gamma_cnt;
     sp.out_cap = (int32_t)L.kc_cap;
     sp.out_blocks_max = (int32_t)L.nc;
-    sp.counters = counters + L.units;
+    sp.counters = counters + L.units * hs::kCounterStride;
     const hipError_t e = hs::launch_select(sp, s);
     if (e != hipSuccess) return from_hip(e);
   }
@@ -231,6 +233,7 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
   sp.ratio = (int32_t)L.ratio;
   sp.n_slots_max = (int32_t)L.fine_slots;
   sp.scores = reinterpret_cast<float*>(ws + L.off_fine_scores);
+  sp.chunk_keys = reinterpret_cast<uint32_t*>(ws + L.off_fine_keys);
   sp.top_k = prm->top_k;
   sp.window = prm->window_tokens;
   sp.out_ids = block_ids;
@@ -256,12 +259,11 @@ hs::DecodeParams decode_params(const hs_kv_cache* kv, const void* q, float scale
   p.ids = block_ids;
   p.counts = num_selected;
   p.max_selected = max_selected;
-  p.blocks_per_split = (int32_t)L.bps;
-  p.max_splits = (int32_t)L.max_splits;
+  p.n_splits = (int32_t)L.n_splits;
   p.part_o = reinterpret_cast<float*>(ws + L.off_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
   p.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
-  p.ready = nullptr;
+  p.score_counters = nullptr;
   p.out = out;
   return p;
 }
@@ -379,13 +381,18 @@ hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, c
   if (st != HS_OK) return st;
   p.dec = decode_params(kv, q, scale, fine->block_size, block_ids, num_selected,
                         prm->max_selected, out, ws + L.off_dec, L.dec);
-  p.ready = reinterpret_cast<int32_t*>(ws + L.off_ready);
-  p.dec.ready = p.ready;
+  if (!hs::step_fits(p.sel.out_blocks_max, p.sel.n_slots_max, p.sel.out_cap)) {
+    // id lists too long for the fused kernel's LDS: the two stages as two
+    // launches, with the same results
+    const hipError_t e = hs::launch_select(p.sel, s);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(hs::launch_decode(p.dec, s));
+  }
+  p.dec.score_counters = p.sel.counters;
   p.units = (int32_t)L.sel.units;
   p.n_chunks = hs::step_chunks(p.sel.n_slots_max);
-  p.n_splits = (int32_t)L.dec.max_splits;
-  p.lookahead = p.units;
-  p.total = p.units * (p.n_chunks + p.n_splits);
+  p.total = p.units * (p.n_chunks + p.dec.n_splits);
+  p.list_cap = p.sel.out_cap;
   return from_hip(hs::launch_step(p, s));
 }
 

@@ -1,4 +1,4 @@
-// decode.hip - stage 3 as one launch: grid (splits, units), one split task
+// decode.hip - stage 3 as one launch: grid (n_splits, units), one split task
 // per workgroup; the unit's last task merges. The device code and its
 // sources are in decode_impl.h.
 #include "decode_impl.h"
@@ -6,57 +6,53 @@
 namespace hs {
 namespace {
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_decode_bf16(DecodeParams p) {
+constexpr int kTargetTasks = 256;  // compute units of the GPU: about one split task each
+
+// One split task: the unit's count is read, its run of ids is copied into LDS
+// (written by an earlier launch, so plain loads), then attention and merge.
+template <typename TE, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
   __shared__ DecodeShared<D, G> ds;
-  decode_task_bf16<D, G>(p, blockIdx.y, blockIdx.x, 0, ds);
+  extern __shared__ int32_t run[];
+  const int unit = blockIdx.y, split = blockIdx.x;
+  int cnt = p.counts[unit];
+  cnt = cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
+  int e0, e1;
+  split_range(cnt, p.n_splits, split, e0, e1);
+  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
+  for (int i = thread_id(); i < e1 - e0; i += kDecThreads) run[i] = ids[e0 + i];
+  __syncthreads();
+  decode_split<TE, D, G>(p, unit, split, run, 0, e1 - e0, ds);
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_decode_f32(DecodeParams p) {
-  __shared__ DecodeShared<D, G> ds;
-  decode_task_f32<D, G, f32_unroll<G>()>(p, blockIdx.y, blockIdx.x, 0, ds);
-}
-
-template <int D>
-hipError_t launch_bf16(const DecodeParams& p, dim3 grid, hipStream_t s) {
+template <typename TE, int D>
+hipError_t launch_g(const DecodeParams& p, dim3 grid, size_t lds, hipStream_t s) {
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_decode_bf16<D, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_decode_bf16<D, 2>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_decode_bf16<D, 4>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_decode_bf16<D, 8>), grid, dim3(256), 0, s, p); break;
-  }
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_f32(const DecodeParams& p, dim3 grid, hipStream_t s) {
-  switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_decode_f32<D, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_decode_f32<D, 2>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_decode_f32<D, 4>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_decode_f32<D, 8>), grid, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_decode<TE, D, 1>), grid, dim3(kDecThreads), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((k_decode<TE, D, 2>), grid, dim3(kDecThreads), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((k_decode<TE, D, 4>), grid, dim3(kDecThreads), lds, s, p); break;
+    default: hipLaunchKernelGGL((k_decode<TE, D, 8>), grid, dim3(kDecThreads), lds, s, p); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// A workgroup takes about 512 tokens (each of its 4 waves a quarter of the
-// blocks), so that every wave pipelines several 32-token stages; long id
-// lists get more blocks per split so that a unit has at most kMaxSplits.
-int decode_blocks_per_split(int block_size, int max_selected) {
-  int bps = block_size >= 128 ? 4 : 4 * ((128 + block_size - 1) / block_size);
-  const int need = (max_selected + kMaxSplits - 1) / kMaxSplits;
-  if (bps < need) bps = (need + 3) / 4 * 4;
-  return bps;
+int decode_splits(int64_t units, int32_t max_selected) {
+  int64_t ns = (kTargetTasks + units - 1) / units;
+  if (ns > max_selected) ns = max_selected;
+  if (ns > kMaxSplits) ns = kMaxSplits;
+  return ns < 1 ? 1 : (int)ns;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  const dim3 grid(p.max_splits, p.kv.batch * p.kv.num_kv_heads);
+  const dim3 grid(p.n_splits, p.kv.batch * p.kv.num_kv_heads);
+  const size_t lds = sizeof(int32_t) * ((p.max_selected + p.n_splits - 1) / p.n_splits);
   if (p.kv.elem_bytes == 2)
-    return p.kv.head_dim == 64 ? launch_bf16<64>(p, grid, s) : launch_bf16<128>(p, grid, s);
-  return p.kv.head_dim == 64 ? launch_f32<64>(p, grid, s) : launch_f32<128>(p, grid, s);
+    return p.kv.head_dim == 64 ? launch_g<bf16_t, 64>(p, grid, lds, s)
+                               : launch_g<bf16_t, 128>(p, grid, lds, s);
+  return p.kv.head_dim == 64 ? launch_g<float, 64>(p, grid, lds, s)
+                             : launch_g<float, 128>(p, grid, lds, s);
 }
 
 }  // namespace hs

@@ -8,15 +8,16 @@
 // compact copy); "SparDA" article section 3.3 (only the selected pages are
 // read) and section 3.4 (one block list shared by every layer).
 //
-// Work split: one task per (unit, split). A workgroup of 4 waves owns a run of
-// blocks_per_split consecutive entries of a unit's id list; each wave takes
-// every fourth entry and keeps an fp32 online-softmax state (m, l, o) for
-// the unit's G query heads. The workgroup combines its waves in LDS, writes
-// one partial per split, and the last workgroup of the unit to finish
-// (arrival counter in the workspace) merges the unit's partials into the
-// output with the log-sum-exp rule, so one launch does the whole stage.
+// Work split: a unit's id list is cut into n_splits equal runs of entries
+// (by the unit's actual count); one workgroup task per (unit, split). The 4
+// waves of a task take every fourth entry of the run and keep an fp32
+// online-softmax state (m, l, o) for the unit's G query heads. The task
+// combines its waves in LDS and publishes one partial; the last task of the
+// unit to arrive (arrival counter in the workspace) merges the n_splits
+// partials into the output with the log-sum-exp rule, so one launch does the
+// whole stage.
 //
-// k_decode_bf16 (bf16 caches): q.k on the matrix cores. For a 16-token tile
+// bf16 caches: q.k on the matrix cores. For a 16-token tile
 // v_mfma_f32_16x16x32_bf16 takes the unit's query heads as rows of A (head j
 // in row 4 (j % 4) + j / 4, so every 16-lane group of the result holds one
 // head's 16 logits) and the K tile as B: each lane's 16-byte load of
@@ -25,8 +26,8 @@
 // wave-uniform; p and the rescale factor go through a small per-wave LDS
 // slice to the p.v accumulation, which runs on the VALU in fp32 with V read
 // as 16-byte rows (lane: 8 dims of one token).
-// k_decode_f32 (float32 caches): all on the VALU; the q.k dot is reduced
-// across the lanes of a token row with DPP.
+// float32 caches: all on the VALU; the q.k dot is reduced across the lanes of
+// a token row with DPP.
 // Logits are kept in base 2: the logit scale is multiplied by log2(e), so
 // exp(l - m) = exp2(l2 - m2) in real arithmetic.
 #pragma once
@@ -37,10 +38,7 @@ namespace hs {
 namespace {
 
 constexpr int kDecWaves = 4;
-// The host keeps the number of splits of a unit at most kMaxSplits (it grows
-// blocks_per_split for very long id lists), so the merge's (m, l) table of
-// 2 * kMaxSplits * G floats fits in the 4 * G * D floats of the wave area.
-constexpr int kMaxSplits = 128;
+constexpr int kDecThreads = kDecWaves * kWave;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
@@ -52,43 +50,79 @@ struct SplitShared {
   int last;
 };
 
-__device__ __forceinline__ int clamp_count(const DecodeParams& p, int unit) {
-  int cnt = published_i32(&p.counts[unit]);
-  return cnt < 0 ? 0 : (cnt > p.max_selected ? p.max_selected : cnt);
+// Entries [e0, e1) of a list of cnt entries owned by split `split` of ns:
+// consecutive runs whose lengths differ by at most one.
+__device__ __forceinline__ void split_range(int cnt, int ns, int split, int& e0, int& e1) {
+  e0 = (int)((int64_t)cnt * split / ns);
+  e1 = (int)((int64_t)cnt * (split + 1) / ns);
 }
 
+// Log-sum-exp merge of the unit's n_splits partials into `out`, by the unit's
+// last-arriving task. Thread t owns output elements t + 256 e of the unit's
+// G x D block; the partials of SB splits are loaded together (one round trip
+// to the device-coherent level per batch), then folded in split order.
 template <int D, int G>
-__device__ __forceinline__ void merge_unit(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns);
-
-// An empty selection has no split to merge: its output rows are zero.
-template <int D, int G>
-__device__ __forceinline__ void write_empty(const DecodeParams& p, int unit) {
+__device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit) {
+  constexpr int E = G * D;
+  constexpr int EPT = (E + kDecThreads - 1) / kDecThreads;
+  constexpr int SB = 16 / EPT;
+  const int tid = thread_id();
+  const int ns = p.n_splits;
+  const int64_t p0 = (int64_t)unit * ns;
+  float m[EPT], l[EPT], o[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+    o[e] = 0.f;
+  }
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+    float ov[SB][EPT], mv[SB][EPT], lv[SB][EPT];
+#pragma unroll
+    for (int bt = 0; bt < SB; ++bt) {
+      const int64_t s = p0 + min(s0 + bt, ns - 1);  // unconditional (clamped) loads overlap
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int idx = min(tid + kDecThreads * e, E - 1), j = idx / D;
+        ov[bt][e] = published(&p.part_o[s * E + idx]);
+        mv[bt][e] = published(&p.part_ml[(s * G + j) * 2]);
+        lv[bt][e] = published(&p.part_ml[(s * G + j) * 2 + 1]);
+      }
+    }
+#pragma unroll
+    for (int bt = 0; bt < SB; ++bt) {
+      if (s0 + bt >= ns) break;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const float mn = fmaxf(m[e], mv[bt][e]);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float a = exp2f(m[e] - ms), c = exp2f(mv[bt][e] - ms);
+        l[e] = l[e] * a + lv[bt][e] * c;
+        o[e] = o[e] * a + ov[bt][e] * c;
+        m[e] = mn;
+      }
+    }
+  }
   const int Hq = p.kv.num_kv_heads * G;
   const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
-  for (int idx = thread_id(); idx < G * D; idx += blockDim.x)
-    p.out[((int64_t)b * Hq + g * G) * D + idx] = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int idx = tid + kDecThreads * e;
+    if (idx < E) p.out[((int64_t)b * Hq + g * G) * D + idx] = l[e] > 0.f ? o[e] / l[e] : 0.f;
+  }
 }
 
-// Arrival of one split task of the unit (of `expected`). The last one clears
-// the unit's ready flag (fused launch: every task of the unit has read it by
-// then) and merges the unit's ns partials.
+// Combine the waves' states (in sh) into the task's partial, publish it and
+// arrive on the unit's counter; the last of the n_splits tasks to arrive
+// merges (and, in the fused launch, clears the unit's scoring counter, which
+// every task of the unit has read by then).
 template <int D, int G>
-__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns,
-                                 int expected) {
-  if (!arrive_last(&p.counters[unit], expected, &sh.last)) return;
-  if (p.ready != nullptr && thread_id() == 0) publish_i32(&p.ready[unit], 0);
-  if (ns == 0) write_empty<D, G>(p, unit);
-  else merge_unit<D, G>(p, sh, unit, ns);
-}
-
-// Combine the waves of this workgroup, publish the split's partial and arrive.
-template <int D, int G>
-__device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int split,
-                             int ns, int expected) {
+__device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<D, G>& sh, int unit,
+                                             int split) {
   const int tid = thread_id();
   __syncthreads();
-  const int64_t ps = (int64_t)unit * p.max_splits + split;
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+  const int64_t ps = (int64_t)unit * p.n_splits + split;
+  for (int idx = tid; idx < G * D; idx += kDecThreads) {
     const int j = idx / D, dd = idx % D;
     float mn = -INFINITY;
 #pragma unroll
@@ -101,107 +135,15 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<
       acc += sh.o[w][j][dd] * a;
       lsum += sh.l[w][j] * a;
     }
-    publish(&p.part_o[(ps * G + j) * D + dd], acc);
+    publish(&p.part_o[ps * G * D + idx], acc);
     if (dd == 0) {
       publish(&p.part_ml[(ps * G + j) * 2 + 0], mn);
       publish(&p.part_ml[(ps * G + j) * 2 + 1], lsum);
     }
   }
-  arrive_and_merge<D, G>(p, sh, unit, ns, expected);
-}
-
-// Log-sum-exp merge of a unit's ns <= kMaxSplits split partials into `out`,
-// by the unit's last-arriving workgroup. Thread t < stride owns output
-// elements t + r * stride of the unit's G x D block (r < R). The (m, l) loads
-// and the first kMergeBatch partial-output loads are issued together, so for
-// the usual split counts the whole merge costs one round trip to the
-// device-coherent level.
-template <int D, int G>
-__device__ __forceinline__ void merge_unit(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int ns) {
-  const int tid = thread_id();
-  constexpr int stride = G * D < 256 ? G * D : 256;
-  constexpr int R = G * D / stride;
-  constexpr int kMergeBatch = 80;
-  float* sm = &sh.o[0][0][0];                 // [ns][G] maxima, then weights
-  float* sl = sm + kMaxSplits * G;            // [ns][G] sums
-  const int64_t p0 = (int64_t)unit * p.max_splits;
-  const int npairs = ns * R;                  // (split, r) loads of this thread
-  const bool owner = tid < stride;
-  float mv = 0.f, lv = 0.f;
-  const bool ml_loader = tid < ns * G;
-  if (ml_loader) {
-    mv = published(&p.part_ml[(p0 * G + tid) * 2]);
-    lv = published(&p.part_ml[(p0 * G + tid) * 2 + 1]);
-  }
-  float v[kMergeBatch];
-#pragma unroll
-  for (int q = 0; q < kMergeBatch; ++q) {
-    const int qq = min(q, npairs - 1);  // unconditional (clamped) loads overlap
-    v[q] = published(&p.part_o[(p0 + qq / R) * G * D + (owner ? tid : 0) + (qq % R) * stride]);
-  }
-  for (int t = tid; t < ns * G; t += blockDim.x) {  // more than 256 (m, l) pairs
-    sm[t] = t == tid ? mv : published(&p.part_ml[(p0 * G + t) * 2]);
-    sl[t] = t == tid ? lv : published(&p.part_ml[(p0 * G + t) * 2 + 1]);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float mn = -INFINITY;
-    for (int s = 0; s < ns; ++s) mn = fmaxf(mn, sm[s * G + tid]);
-    sh.m[0][tid] = mn == -INFINITY ? 0.f : mn;
-  }
-  __syncthreads();
-  for (int t = tid; t < ns * G; t += blockDim.x) sm[t] = exp2f(sm[t] - sh.m[0][t % G]);
-  __syncthreads();
-  if (tid < G) {
-    float lsum = 0.f;
-    for (int s = 0; s < ns; ++s) lsum += sl[s * G + tid] * sm[s * G + tid];
-    sh.l[0][tid] = lsum;
-  }
-  __syncthreads();
-  if (!owner) return;
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int q = 0; q < kMergeBatch; ++q)
-    if (q < npairs) acc[q % R] += v[q] * sm[(q / R) * G + (tid + (q % R) * stride) / D];
-  for (int q = kMergeBatch; q < npairs; ++q)  // long id lists only
-    acc[q % R] += published(&p.part_o[(p0 + q / R) * G * D + tid + (q % R) * stride]) *
-                  sm[(q / R) * G + (tid + (q % R) * stride) / D];
-  const int Hq = p.kv.num_kv_heads * G;
-  const int b = unit / p.kv.num_kv_heads, g = unit % p.kv.num_kv_heads;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int idx = tid + r * stride, j = idx / D;
-    const float lsum = sh.l[0][j];
-    p.out[((int64_t)b * Hq + g * G) * D + idx] = lsum > 0.f ? acc[r] / lsum : 0.f;
-  }
-}
-
-// Entries [e0, e1) of the unit's id list that split task `split` owns, and
-// the unit's split count ns. A task with no entry returns false: in a
-// separate launch (expected == 0, ns arrivals) it only writes the zero output
-// of an empty selection; in a fused launch every task arrives (expected of
-// them), so the last one still merges.
-struct SplitSpan {
-  int ns, e0, e1;
-};
-
-template <int D, int G>
-__device__ __forceinline__ bool split_span(const DecodeParams& p, SplitShared<D, G>& sh, int unit, int split,
-                           int expected, SplitSpan& sp) {
-  const int cnt = clamp_count(p, unit);
-  const int bps = p.blocks_per_split;
-  sp.ns = (cnt + bps - 1) / bps;
-  sp.e0 = split * bps;
-  sp.e1 = min(sp.e0 + bps, cnt);
-  if (sp.e0 < cnt) return true;
-  if (expected == 0) {
-    if (cnt == 0 && split == 0) write_empty<D, G>(p, unit);
-  } else {
-    arrive_and_merge<D, G>(p, sh, unit, sp.ns, expected);
-  }
-  return false;
+  if (!arrive_last(counter_of(p.counters, unit), p.n_splits, &sh.last)) return;
+  if (p.score_counters != nullptr && tid == 0) publish_i32(counter_of(p.score_counters, unit), 0);
+  merge_splits<D, G>(p, unit);
 }
 
 // --------------------------------------------------------------- bf16 path
@@ -225,10 +167,12 @@ struct DecodeShared {
   int st_len[kDecWaves][kStagesPerChunk];
 };
 
-// One split task of a bf16 cache; expected: see split_span.
+// Attention of the unit's query heads over the blocks ids[e0 .. e1) (a list
+// in LDS or global memory) of a bf16 cache; leaves each wave's state in
+// ds.sh for finish_split.
 template <int D, int G>
-__device__ __forceinline__ void decode_task_bf16(const DecodeParams& p, int unit, int split, int expected,
-                                 DecodeShared<D, G>& ds) {
+__device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, const int32_t* ids,
+                                            int e0, int e1, DecodeShared<D, G>& ds) {
   constexpr int KC = D / 32;       // MFMA k-chunks per token row
   constexpr int VL = D / 8;        // lanes per V row (16 bytes each)
   constexpr int TPV = kWave / VL;  // tokens per V load instruction
@@ -242,9 +186,6 @@ __device__ __forceinline__ void decode_task_bf16(const DecodeParams& p, int unit
   auto& st_len = ds.st_len;
 
   const KvView& kv = p.kv;
-  SplitSpan span;
-  if (!split_span<D, G>(p, sh, unit, split, expected, span)) return;
-  const int e0 = span.e0, e1 = span.e1, ns = span.ns;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int T = clamp_len(kv, b);
   const int S = p.block_size;
@@ -376,12 +317,11 @@ __device__ __forceinline__ void decode_task_bf16(const DecodeParams& p, int unit
   const int first = e0 + wave;
   const int nent = first < e1 ? (e1 - first + kDecWaves - 1) / kDecWaves : 0;
   const int nst = nent * spe;
-  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
   for (int c0 = 0; c0 < nst; c0 += kStagesPerChunk) {
     const int cst = min(kStagesPerChunk, nst - c0);
     if (lane < cst) {
       const int st = c0 + lane, i = st / spe, sub = st % spe;
-      const int beta = published_i32(&ids[first + kDecWaves * i]);
+      const int beta = ids[first + kDecWaves * i];
       int64_t base = 0;
       int len = 0;
       if ((unsigned)beta < (unsigned)nb) {
@@ -441,22 +381,19 @@ __device__ __forceinline__ void decode_task_bf16(const DecodeParams& p, int unit
       }
     }
   }
-  finish_split<D, G>(p, sh, unit, split, ns, expected ? expected : ns);
 }
 
 // -------------------------------------------------------------- float32 path
-// One split task of a float32 cache; expected: see split_span.
+// Attention over ids[e0 .. e1) for a float32 cache; leaves each wave's state
+// in ds.sh for finish_split.
 template <int D, int G, int UNR>
-__device__ __forceinline__ void decode_task_f32(const DecodeParams& p, int unit, int split, int expected,
-                                DecodeShared<D, G>& ds) {
+__device__ __forceinline__ void attend_f32(const DecodeParams& p, int unit, const int32_t* ids,
+                                           int e0, int e1, DecodeShared<D, G>& ds) {
   constexpr int EPL = 4;              // floats per 16-byte load
   constexpr int LPT = D / EPL;        // lanes per token row
   constexpr int TPW = kWave / LPT;    // tokens per wave instruction
   SplitShared<D, G>& sh = ds.sh;
   const KvView& kv = p.kv;
-  SplitSpan span;
-  if (!split_span<D, G>(p, sh, unit, split, expected, span)) return;
-  const int e0 = span.e0, e1 = span.e1, ns = span.ns;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int T = clamp_len(kv, b);
   const int S = p.block_size;
@@ -483,9 +420,8 @@ __device__ __forceinline__ void decode_task_f32(const DecodeParams& p, int unit,
 #pragma unroll
     for (int k = 0; k < EPL; ++k) o[j][k] = 0.f;
   }
-  const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
   for (int e = e0 + wave; e < e1; e += kDecWaves) {
-    const int beta = published_i32(&ids[e]);
+    const int beta = ids[e];
     if ((unsigned)beta >= (unsigned)nb) continue;  // wave-uniform
     const int tb = beta * S, te = min(tb + S, T);
     for (int t0 = tb; t0 < te; t0 += TPW * UNR) {  // wave-uniform trip count
@@ -575,12 +511,22 @@ __device__ __forceinline__ void decode_task_f32(const DecodeParams& p, int unit,
       }
     }
   }
-  finish_split<D, G>(p, sh, unit, split, ns, expected ? expected : ns);
 }
 
 // Unroll of the float32 path's token loop (registers bound it at G = 8).
 template <int G>
 constexpr int f32_unroll() { return G == 8 ? 4 : 8; }
+
+// Attention of one split task over ids[e0 .. e1), then its partial and
+// arrival (the last task of the unit merges).
+template <typename TE, int D, int G>
+__device__ __forceinline__ void decode_split(const DecodeParams& p, int unit, int split,
+                                             const int32_t* ids, int e0, int e1,
+                                             DecodeShared<D, G>& ds) {
+  if constexpr (sizeof(TE) == 2) attend_bf16<D, G>(p, unit, ids, e0, e1, ds);
+  else attend_f32<D, G, f32_unroll<G>()>(p, unit, ids, e0, e1, ds);
+  finish_split<D, G>(p, ds.sh, unit, split);
+}
 
 }  // namespace
 }  // namespace hs

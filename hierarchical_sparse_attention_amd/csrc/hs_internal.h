@@ -124,6 +124,14 @@ __device__ __forceinline__ void publish_i32(int32_t* p, int32_t v) {
 __device__ __forceinline__ int32_t published_i32(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Arrival counters and flags that workgroups poll or update live one per
+// 256-byte line (kCounterStride int32s apart), so that pollers of different
+// units hit different memory channels.
+constexpr int kCounterStride = 64;
+__device__ __forceinline__ int32_t* counter_of(int32_t* base, int unit) {
+  return base + (int64_t)unit * kCounterStride;
+}
+
 // Every thread calls this; returns true in every thread of the workgroup that
 // arrived last (of `expected`) on `counter`, which it then resets to zero.
 __device__ __forceinline__ bool arrive_last(int32_t* counter, int expected, int* flag) {
@@ -184,6 +192,7 @@ struct SelectParams {
   int32_t gamma_cap, ratio;  // R = C / S
   int32_t n_slots_max;       // scores row length
   float* scores;             // [units][n_slots_max]
+  uint32_t* chunk_keys;      // [units][chunks][2]: largest order key, largest ~key of a chunk
   int32_t top_k;
   int32_t window;            // tokens (0 = none)
   int32_t* out_ids;          // [units][out_cap]
@@ -193,6 +202,7 @@ struct SelectParams {
   int32_t* counters;         // [units] workgroup arrivals; zero between calls
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
+// Dynamic LDS of a selection workgroup: bitmap words, then keys (general path).
 size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max);
 
 struct DecodeParams {
@@ -201,28 +211,34 @@ struct DecodeParams {
   int32_t G;
   float scale_log2;          // scale * log2(e)
   int32_t block_size;
-  const int32_t* ids;
-  const int32_t* counts;
+  const int32_t* ids;        // [units][max_selected] (separate launch)
+  const int32_t* counts;     // [units]
   int32_t max_selected;
-  int32_t blocks_per_split, max_splits;
-  float* part_o;             // [units][max_splits][G][d]
-  float* part_ml;            // [units][max_splits][G][2]
+  int32_t n_splits;          // split tasks per unit (<= kMaxSplits)
+  float* part_o;             // [units][n_splits][G][d]
+  float* part_ml;            // [units][n_splits][G][2]
   int32_t* counters;         // [units] split arrivals; zero between calls
-  int32_t* ready;            // fused launch: [units] selection-done flags, else null
+  int32_t* score_counters;   // fused launch: [units] scoring arrivals to clear, else null
   float* out;                // [B][Hq][d]
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-int decode_blocks_per_split(int block_size, int max_selected);
+constexpr int kMaxSplits = 128;
+// Split tasks per unit: enough to give every compute unit of the GPU about
+// one task (the work of a unit is its id list), at most one per selectable
+// block and at most kMaxSplits.
+int decode_splits(int64_t units, int32_t max_selected);
 
 // Fused last selection level + decode of one layer (one persistent launch).
 struct StepParams {
   SelectParams sel;          // the last (or only) selection level
-  DecodeParams dec;          // ids / counts = sel.out_ids / sel.out_cnt
-  int32_t* ready;            // [units] selection-done flags; zero between calls
-  int32_t units, n_chunks, n_splits, lookahead, total;
+  DecodeParams dec;          // counts / out / workspace of the decode
+  int32_t units, n_chunks, total;
+  int32_t list_cap;          // LDS id list entries (= sel.out_cap)
 };
 hipError_t launch_step(const StepParams& p, hipStream_t s);
 int step_chunks(int32_t n_slots_max);  // scoring tasks per unit
+// Whether the fused kernel's LDS (bitmap, keys, id list) fits for these sizes.
+bool step_fits(int32_t out_blocks_max, int32_t n_slots_max, int32_t list_cap);
 
 constexpr int kMaxBlocks = 32768;  // blocks per unit of a summary level (LDS bitmap)
 

@@ -34,7 +34,8 @@ hipError_t launch_k(const SelectParams& p, dim3 grid, size_t lds, hipStream_t s)
 
 size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max) {
   const size_t words = (size_t)(out_blocks_max + 31) / 32;
-  const size_t keys = n_slots_max <= kLdsKeys ? (size_t)n_slots_max : 0;
+  const bool general = n_slots_max > kThreads * kRegKeys;
+  const size_t keys = general && n_slots_max <= kLdsKeys ? (size_t)n_slots_max : 0;
   return sizeof(uint32_t) * (words + keys);
 }
 

@@ -15,15 +15,16 @@
 //    box, since max(q m, q M) = m min(q,0) + M max(q,0)), so each summary
 //    element costs one FMA whatever G is. A row is read by LPR lanes with
 //    16-byte loads and reduced across them with DPP; fp32 scores go to the
-//    workspace.
-//  * top-k - the unit's last workgroup to finish scoring (arrival counter in
-//    the workspace) selects. Exact radix select on order-preserving uint32
-//    keys of the fp32 scores: the leading bits shared by every key are
-//    skipped, then 11-bit digits are resolved with an LDS histogram until
-//    the k-th largest key is known. Keys above it are kept; keys equal to it
-//    are kept in ascending candidate order (candidate order is ascending
-//    block order), which is the lowest-index tie-break. Kept blocks and the
-//    window's blocks are set in an LDS bitmap, written out as ascending ids.
+//    workspace with device-coherent stores.
+//  * top-k - one workgroup reads the unit's published scores and selects.
+//    Exact radix select on order-preserving uint32 keys of the fp32 scores:
+//    the leading bits shared by every key are skipped and the next 11-bit
+//    digit is resolved with an LDS histogram; this usually narrows the k-th
+//    largest key to a bin of a few keys, which are then ranked directly
+//    (key descending, candidate index ascending: the lowest-index
+//    tie-break); a crowded bin takes further 11-bit passes. Kept blocks and
+//    the window's blocks are set in an LDS bitmap and written out as
+//    ascending ids (to LDS, to global memory, or both).
 #pragma once
 
 #include <type_traits>
@@ -43,6 +44,12 @@ constexpr int kBins = 1 << kDigitBits;
 constexpr int kBinsPerThread = kBins / kThreads;
 constexpr int kRegKeys = 16;    // keys per thread of the register path (<= 4096 candidates)
 constexpr int kLdsKeys = 8192;  // beyond this many candidates keys stay in the workspace
+constexpr int kMaxCand = 128;   // a threshold bin this small is ranked directly
+
+// Number of scoring tasks of a unit for a level with n_slots_max candidates.
+__host__ __device__ inline int select_chunks(int n_slots_max) {
+  return (n_slots_max + kRowsPerWG - 1) / kRowsPerWG;
+}
 
 // slot c -> block id (or -1 if the slot holds no candidate)
 struct SlotMap {
@@ -57,19 +64,31 @@ struct SlotMap {
   }
 };
 
-__device__ __forceinline__ SlotMap make_slots(const SelectParams& p, int unit, int nb) {
-  SlotMap m;
-  m.nb = nb;
-  m.ratio = p.ratio;
-  m.gamma = nullptr;
-  m.gcnt = 0;
+// What a unit looks like to one selection level: T (clamped), its number of
+// blocks nb, its candidate slots and their count n.
+struct UnitGeom {
+  int T, nb, n;
+  SlotMap slots;
+};
+
+__device__ __forceinline__ UnitGeom unit_geom(const SelectParams& p, int unit) {
+  UnitGeom u;
+  u.T = clamp_len(p.kv, unit / p.kv.num_kv_heads);
+  const int nb = (u.T + p.block_size - 1) / p.block_size;
+  u.nb = nb < p.out_blocks_max ? nb : p.out_blocks_max;
+  u.slots.nb = u.nb;
+  u.slots.ratio = p.ratio;
+  u.slots.gamma = nullptr;
+  u.slots.gcnt = 0;
   if (p.gamma) {
     int gc = p.gamma_cnt[unit];
     gc = gc < 0 ? 0 : (gc > p.gamma_cap ? p.gamma_cap : gc);
-    m.gamma = p.gamma + (int64_t)unit * p.gamma_cap;
-    m.gcnt = gc;
+    u.slots.gamma = p.gamma + (int64_t)unit * p.gamma_cap;
+    u.slots.gcnt = gc;
   }
-  return m;
+  const int n = p.gamma ? u.slots.gcnt * p.ratio : u.nb;
+  u.n = n < p.n_slots_max ? n : p.n_slots_max;
+  return u;
 }
 
 template <typename TE>
@@ -79,12 +98,16 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i) {
 }
 
 struct TopkShared {
-  uint32_t hist[kBins];
+  __attribute__((aligned(16))) uint32_t hist[kBins];
+  uint32_t cand_key[kWaves][kMaxCand];   // threshold-bin keys (up to kMaxCand + 7 read)
+  int32_t cand_slot[kWaves][kMaxCand];
   uint32_t tie_cnt[kRegKeys][kWaves];
+  __attribute__((aligned(16))) uint32_t scan_tot[3][kWaves];  // wave totals of three scans
   float stage[kRowsPerWG];                     // scores of this workgroup's rows
-  uint32_t wave_tot[kWaves];
+  __attribute__((aligned(16))) uint32_t wave_tot[kWaves];
   uint32_t red[3][kWaves];
-  uint32_t bcast[4];
+  __attribute__((aligned(16))) uint32_t bcast[4];
+  __attribute__((aligned(16))) uint32_t wcnt[kWaves];
   int last;
 };
 
@@ -158,10 +181,9 @@ __device__ __forceinline__ int hist_slot(uint32_t b) { return (int)((b & 7u) * k
 // Digit search of one radix pass over the LDS histogram: thread t owns the
 // logical bins nbins-1-8t down to nbins-8-8t; exactly one bin d has
 // above(d) < remaining <= above(d) + hist[d]. Updates prefix and remaining in
-// every thread and returns hist[d] (after the last pass: the number of keys
-// equal to the threshold).
+// every thread and returns hist[d], the number of keys in the bin.
 __device__ __forceinline__ uint32_t take_digit(TopkShared& sh, int nbins, int shift, uint32_t& prefix,
-                               uint32_t& remaining) {
+                                               uint32_t& remaining) {
   const int tid = thread_id();
   uint32_t h[kBinsPerThread], local = 0;
 #pragma unroll
@@ -189,179 +211,433 @@ __device__ __forceinline__ uint32_t take_digit(TopkShared& sh, int nbins, int sh
   return in_bin;
 }
 
-// Window blocks into the bitmap, then the bitmap as ascending ids. Ids and
-// count are written with device-coherent stores, so that a workgroup of the
-// same launch on another XCD can read them once this one has drained them.
-__device__ __forceinline__ void emit_ids(const SelectParams& p, int unit, int T, int nb, uint32_t* bitmap,
-                         TopkShared& sh) {
-  const int tid = thread_id();
-  const int S = p.block_size;
-  const int words = (nb + 31) / 32;
-  if (p.window > 0) {
-    const int64_t lo_tok = (int64_t)T - p.window;
-    const int w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / S);
-    for (int beta = w0 + tid; beta < nb; beta += kThreads)
-      atomicOr(&bitmap[beta >> 5], 1u << (beta & 31));
-  }
-  __syncthreads();
-  // thread t owns bitmap words [t*wpt, (t+1)*wpt)
-  const int wpt = (words + kThreads - 1) / kThreads;
-  const int w0 = tid * wpt, w1 = min(w0 + wpt, words);
-  uint32_t ones = 0;
-  for (int w = w0; w < w1; ++w) ones += __popc(bitmap[w]);
-  uint32_t total;
-  uint32_t pos = block_excl_scan(ones, &total, sh);
-  int32_t* ids = p.out_ids + (int64_t)unit * p.out_cap;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t m = bitmap[w];
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      if (pos < (uint32_t)p.out_cap) publish_i32(&ids[pos], w * 32 + bit);
-      ++pos;
-    }
-  }
-  if (tid == 0) publish_i32(&p.out_cnt[unit], (int32_t)min(total, (uint32_t)p.out_cap));
+__device__ __forceinline__ void mark(uint32_t* bitmap, int beta) {
+  atomicOr(&bitmap[beta >> 5], 1u << (beta & 31));
 }
 
-// Fast path for units with at most kThreads * KPT candidates: thread t keeps
-// the keys of candidates c = u * kThreads + t (u < KPT) in registers, so the
-// published scores are read with coalesced loads and the histogram passes
-// touch LDS only for the histogram. Ties at the threshold are ranked in
-// ascending candidate order with per-slot wave ballots.
-template <int KPT>
-__device__ __forceinline__ void select_unit_regs(const SelectParams& p, int unit, int T, const SlotMap& slots,
-                                 int n, TopkShared& sh, uint32_t* bitmap) {
+// Exclusive prefix sum over the workgroup in thread order without a trailing
+// barrier: tot4 (4 words of LDS, 16-byte aligned) holds the wave totals and
+// must not be rewritten before every thread has passed a later barrier.
+// *total gets the workgroup's sum.
+__device__ __forceinline__ uint32_t wg_excl_scan(uint32_t x, uint32_t* tot4, uint32_t* total) {
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
-  const int nb = slots.nb;
+  const uint32_t inc = wave_incl_scan(x);
+  if (lane == kWave - 1) tot4[wave] = inc;
+  __syncthreads();
+  const uint4 t = *reinterpret_cast<const uint4*>(tot4);
+  *total = t.x + t.y + t.z + t.w;
+  return inc - x + (wave > 0 ? t.x : 0u) + (wave > 1 ? t.y : 0u) + (wave > 2 ? t.z : 0u);
+}
+
+// Digit search of a radix pass over the plain-layout LDS histogram: thread t
+// owns the logical bins nbins-1-8t down to nbins-8-8t (two 16-byte loads); a
+// workgroup scan of the threads' sums gives the count above each thread's
+// bins, and the one thread holding the bin d with
+// above(d) < remaining <= above(d) + hist[d] broadcasts it (the search
+// itself is branch-free). Updates prefix and remaining in every thread and
+// returns hist[d].
+__device__ __forceinline__ uint32_t take_digit_flat(TopkShared& sh, int nbins, int shift,
+                                                    uint32_t& prefix, uint32_t& remaining) {
+  const int tid = thread_id();
+  const int top = nbins - kBinsPerThread * tid;  // this thread's bins: [top - 8, top)
+  uint32_t h[kBinsPerThread];
+  if (nbins >= kBinsPerThread) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (top > 0) {
+      a = *reinterpret_cast<const uint4*>(&sh.hist[top - 8]);
+      b = *reinterpret_cast<const uint4*>(&sh.hist[top - 4]);
+    }
+    h[0] = b.w; h[1] = b.z; h[2] = b.y; h[3] = b.x;
+    h[4] = a.w; h[5] = a.z; h[6] = a.y; h[7] = a.x;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) h[i] = top - 1 - i >= 0 ? sh.hist[top - 1 - i] : 0u;
+  }
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) local += h[i];
+  uint32_t tot;
+  uint32_t run = wg_excl_scan(local, sh.scan_tot[0], &tot);
+  int hit = -1;
+  uint32_t hit_above = 0, hit_h = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    const bool here = run < remaining && run + h[i] >= remaining;
+    hit = here ? i : hit;
+    hit_above = here ? run : hit_above;
+    hit_h = here ? h[i] : hit_h;
+    run += h[i];
+  }
+  if (hit >= 0) {
+    sh.bcast[0] = (uint32_t)(top - 1 - hit);
+    sh.bcast[1] = hit_above;
+    sh.bcast[2] = hit_h;
+  }
+  __syncthreads();
+  const uint4 bc = *reinterpret_cast<const uint4*>(sh.bcast);
+  prefix |= bc.x << shift;
+  remaining -= bc.y;
+  return bc.z;
+}
+
+// Top-k, window and ascending ids of a single-level unit with at most
+// kThreads * kRegKeys candidates (candidate c is block c), to `list` (LDS)
+// and/or `gids` / `*gcnt` (global). Thread t owns the contiguous candidates
+// c = kRegKeys * t + u (u < kRegKeys), keys in registers, so candidate order
+// is thread order and every "rank in block order" below is one workgroup
+// scan of a per-thread count. The key range comes with the scores (the
+// scoring tasks publish each chunk's largest key and ~key), so the first
+// radix pass starts right after the loads. Kept candidates (above the
+// threshold, ranked into the top-k inside the threshold bin, or in the
+// window) are bits of a per-thread mask. On this hardware a dependent LDS
+// round trip costs about as much as 15 VALU instructions, so LDS reads are
+// batched and per-key work is kept branch-free.
+__device__ __forceinline__ int topk_single(const SelectParams& p, int unit, const UnitGeom& ug,
+                                           TopkShared& sh, int32_t* list, int32_t* gids,
+                                           int32_t* gcnt) {
+  constexpr int KPT = kRegKeys;
+  const int tid = thread_id();
+  const int n = ug.n;
+  const int c0 = KPT * tid;  // first candidate of this thread
   const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
-  for (int w = tid; w < (nb + 31) / 32; w += kThreads) bitmap[w] = 0u;
+  float v[KPT];
+  uint32_t kmax = 0, kmin_inv = 0;
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)  // unconditional (clamped) loads that overlap
+      v[u] = published(&sc[min(c0 + u, n - 1)]);
+    const int nch = (n + kRowsPerWG - 1) / kRowsPerWG;
+    const int32_t* ck = reinterpret_cast<const int32_t*>(
+        p.chunk_keys + (int64_t)unit * select_chunks(p.n_slots_max) * 2);
+#pragma unroll
+    for (int ch = 0; ch < KPT; ++ch) {
+      const int cc = min(ch, nch - 1);
+      kmax = max(kmax, (uint32_t)published_i32(&ck[2 * cc]));
+      kmin_inv = max(kmin_inv, (uint32_t)published_i32(&ck[2 * cc + 1]));
+    }
+  }
+  for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+  int w0 = ug.nb;  // blocks w0 .. nb-1 hold the window's tokens
+  if (p.window > 0) {
+    const int64_t lo_tok = (int64_t)ug.T - p.window;
+    w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / p.block_size);
+  }
+  // keys; candidates past n get key 0 (below every finite score's key)
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const uint32_t bits = __float_as_uint(v[u] + 0.f);  // -0 -> +0
+    const uint32_t k = bits ^ ((uint32_t)((int32_t)bits >> 31) | 0x80000000u);
+    kr[u] = c0 + u < n ? k : 0u;
+  }
+  const uint32_t kmin = ~kmin_inv;
+  const uint32_t n_valid = n > 0 ? (uint32_t)n : 0u;
+  const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
+  // threshold bin [prefix, pmax]: keys above it are kept, `remaining` of its
+  // in_bin keys are kept (ranked by key, then candidate index)
+  uint32_t prefix = 0xFFFFFFFFu, pmax = 0xFFFFFFFFu, remaining = 0, in_bin = 0;
+  int resolved = 32;
+  bool keep_all = false;
+  if (k_eff == n_valid && k_eff > 0) {
+    keep_all = true;
+  } else if (k_eff > 0) {
+    __syncthreads();  // histogram cleared
+    remaining = k_eff;
+    if (kmax == kmin) {
+      prefix = kmax;
+      in_bin = n_valid;
+    } else {
+      resolved = __clz(kmax ^ kmin);  // < 32 here
+      prefix = resolved == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> resolved));
+      for (bool first = true;; first = false) {
+        const int db = min(kDigitBits, 32 - resolved);
+        const int shift = 32 - resolved - db;
+        const uint32_t dmask = (1u << db) - 1u;
+        if (first) {
+          // every present key shares the leading `resolved` bits: no test
+#pragma unroll
+          for (int u = 0; u < KPT; ++u)
+            if (kr[u] != 0) atomicAdd(&sh.hist[(kr[u] >> shift) & dmask], 1u);
+        } else {
+          const uint32_t hi_pre = prefix >> (32 - resolved);
+#pragma unroll
+          for (int u = 0; u < KPT; ++u)
+            if (kr[u] != 0 && (kr[u] >> (32 - resolved)) == hi_pre)
+              atomicAdd(&sh.hist[(kr[u] >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        in_bin = take_digit_flat(sh, 1 << db, shift, prefix, remaining);
+        resolved += db;
+        if (in_bin == remaining || in_bin <= (uint32_t)kMaxCand || resolved == 32) break;
+        for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+        __syncthreads();
+      }
+    }
+    pmax = prefix | (resolved >= 32 ? 0u : (0xFFFFFFFFu >> resolved));
+  }
+  const bool take_bin = in_bin > 0 && in_bin == remaining;
+  const bool rank_bin = !keep_all && !take_bin && in_bin > 0;
+  // bit u of keep / inb: candidate c0 + u is kept / in the threshold bin
+  uint32_t keep = 0, inb = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int c = c0 + u;
+    const uint32_t k = kr[u];
+    const bool in = k != 0 && k >= prefix && k <= pmax;
+    const bool kept = c < n && (keep_all || c >= w0 || k > pmax || (take_bin && in));
+    keep |= (uint32_t)kept << u;
+    inb |= (uint32_t)(rank_bin && in) << u;
+  }
+  if (rank_bin) {  // uniform
+    uint32_t m;
+    uint32_t pos = wg_excl_scan((uint32_t)__popc(inb), sh.scan_tot[1], &m);  // m == in_bin
+    if (resolved == 32) {
+      // every bin key equals the threshold: the first `remaining` of them in
+      // candidate order are kept
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if ((inb >> u) & 1u) keep |= (pos++ < remaining ? 1u : 0u) << u;
+    } else {
+      // a few distinct keys: gather them in candidate order, then each owner
+      // ranks its own bin keys (key desc, candidate asc) against all of them
+      uint32_t* ckey = &sh.cand_key[0][0];
+      int32_t* cslot = &sh.cand_slot[0][0];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if ((inb >> u) & 1u) {
+          ckey[pos] = kr[u];
+          cslot[pos] = c0 + u;
+          ++pos;
+        }
+      __syncthreads();
+      if (inb) {  // this thread's bin keys, ranked against the first 16 then the rest
+        uint32_t kj[16];
+        int cj[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          kj[i] = ckey[i];
+          cj[i] = cslot[i];
+        }
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          if (!((inb >> u) & 1u)) continue;
+          const uint32_t kt = kr[u];
+          const int ct = c0 + u;
+          uint32_t rank = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            rank += ((uint32_t)i < m && (kj[i] > kt || (kj[i] == kt && cj[i] < ct))) ? 1u : 0u;
+          for (uint32_t j = 16; j < m; ++j) {  // crowded bins only
+            const uint32_t k2 = ckey[j];
+            const int c2 = cslot[j];
+            rank += (k2 > kt || (k2 == kt && c2 < ct)) ? 1u : 0u;
+          }
+          if (rank < remaining) keep |= 1u << u;
+        }
+      }
+    }
+  }
+  // ascending ids: a kept block's position is its rank in candidate order
+  uint32_t total;
+  uint32_t at = wg_excl_scan((uint32_t)__popc(keep), sh.scan_tot[2], &total);
+  const uint32_t cap = (uint32_t)p.out_cap;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if ((keep >> u) & 1u) {
+      if (at < cap) {
+        if (list) list[at] = c0 + u;
+        if (gids) gids[at] = c0 + u;
+      }
+      ++at;
+    }
+  const int cnt = (int)min(total, cap);
+  if (gcnt && tid == 0) *gcnt = cnt;
+  __syncthreads();  // the list is complete; scan slots may be reused
+  return cnt;
+}
+
+// Top-k of a unit whose candidates fit in registers (n <= kThreads * kRegKeys):
+// thread t keeps the keys of candidates c = u * kThreads + t (u < kRegKeys),
+// so the published scores are read with coalesced loads and the histogram
+// passes touch LDS only for the histogram. TWO: candidate slots map to fine
+// blocks through the kept coarse blocks (else slot c is block c). Sets the
+// kept blocks in `bitmap` (zeroed by the caller); every path has a barrier
+// before its first mark.
+template <bool TWO>
+__device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const UnitGeom& ug,
+                                          TopkShared& sh, uint32_t* bitmap) {
+  constexpr int KPT = kRegKeys;
+  const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
+  const int n = ug.n;
+  if (n <= 0) {  // uniform
+    __syncthreads();
+    return;
+  }
+  auto block_of = [&](int c) { return TWO ? ug.slots.block_of(c) : c; };
+  const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
   float v[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u)  // unconditional (clamped), coalesced loads that overlap
     v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
+  // the first histogram is cleared while the loads are in flight
+  for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
   uint32_t kr[KPT];
-  uint32_t cnt = 0, kmax = 0, kmin = 0xFFFFFFFFu;
+  uint32_t cnt = 0, kmax = 0, kmin_inv = 0;  // kmin_inv: largest ~key
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
     const int c = u * kThreads + tid;
-    const uint32_t k = (c < n && slots.block_of(c) >= 0) ? order_key(v[u]) : 0u;
+    const bool ok = c < n && (!TWO || ug.slots.block_of(c) >= 0);
+    const uint32_t k = ok ? order_key(v[u]) : 0u;
     kr[u] = k;
-    if (k) {
-      ++cnt;
-      kmax = max(kmax, k);
-      kmin = min(kmin, k);
-    }
+    kmax = max(kmax, k);
+    kmin_inv = max(kmin_inv, ok ? ~k : 0u);
+    if (TWO) cnt += ok ? 1u : 0u;
   }
-  cnt = wave_sum_u(cnt);
   kmax = wave_max_u(kmax);
-  kmin = wave_min_u(kmin);
+  kmin_inv = wave_max_u(kmin_inv);
+  if (TWO) cnt = wave_sum_u(cnt);
   if (lane == 0) {
     sh.red[0][wave] = cnt;
     sh.red[1][wave] = kmax;
-    sh.red[2][wave] = kmin;
+    sh.red[2][wave] = kmin_inv;
   }
   __syncthreads();
-  uint32_t n_valid = 0;
+  uint32_t n_valid = TWO ? 0u : (uint32_t)n;
   kmax = 0;
-  kmin = 0xFFFFFFFFu;
+  kmin_inv = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    n_valid += sh.red[0][w];
+    if (TWO) n_valid += sh.red[0][w];
     kmax = max(kmax, sh.red[1][w]);
-    kmin = min(kmin, sh.red[2][w]);
+    kmin_inv = max(kmin_inv, sh.red[2][w]);
   }
+  const uint32_t kmin = ~kmin_inv;
   const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
-  const bool keep_none = k_eff == 0;
-  bool keep_all = !keep_none && k_eff == n_valid;
-  uint32_t thr = 0, ties_keep = 0, ties_total = 0;
-  if (!keep_none && !keep_all && kmax == kmin) {
-    thr = kmax;
-    ties_keep = k_eff;
-    ties_total = n_valid;
-  } else if (!keep_none && !keep_all) {
-    const int common = __clz(kmax ^ kmin);  // < 32 here
-    int shift = 32 - common;
-    uint32_t prefix = common == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> common));
-    uint32_t remaining = k_eff;
-    while (shift > 0) {
-      const int db = shift < kDigitBits ? shift : kDigitBits;
-      shift -= db;
-      const int hi = shift + db;
+  if (k_eff == 0) return;
+  if (k_eff == n_valid) {  // every candidate is kept
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (kr[u]) mark(bitmap, block_of(u * kThreads + tid));
+    return;
+  }
+  // Threshold: after the loop every key > pmax is kept, every key < prefix is
+  // dropped, and `remaining` of the in_bin keys in [prefix, pmax] are kept.
+  uint32_t prefix, remaining = k_eff, in_bin;
+  int resolved;  // leading key bits fixed in prefix
+  if (kmax == kmin) {
+    prefix = kmax;
+    resolved = 32;
+    in_bin = n_valid;
+  } else {
+    resolved = __clz(kmax ^ kmin);  // < 32 here
+    prefix = resolved == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> resolved));
+    for (;;) {
+      const int db = min(kDigitBits, 32 - resolved);
+      const int shift = 32 - resolved - db;
       const uint32_t dmask = (1u << db) - 1u;
-      for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         const uint32_t k = kr[u];
-        if (k != 0 && (hi >= 32 || (k >> hi) == (prefix >> hi)))
+        if (k != 0 && (resolved == 0 || (k >> (32 - resolved)) == (prefix >> (32 - resolved))))
           atomicAdd(&sh.hist[hist_slot((k >> shift) & dmask)], 1u);
       }
       __syncthreads();
-      ties_total = take_digit(sh, 1 << db, shift, prefix, remaining);
+      in_bin = take_digit(sh, 1 << db, shift, prefix, remaining);
+      resolved += db;
+      if (in_bin == remaining || in_bin <= (uint32_t)kMaxCand || resolved == 32) break;
+      for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+      __syncthreads();
     }
-    thr = prefix;
-    ties_keep = remaining;
   }
-  // every key equal to the threshold is kept (the usual case): no ranking needed
-  const bool all_ties = !keep_none && !keep_all && ties_keep == ties_total;
-  if (!keep_none && (keep_all || all_ties)) {
+  const uint32_t pmax = prefix | (resolved >= 32 ? 0u : (0xFFFFFFFFu >> resolved));
+  const bool take_bin = in_bin == remaining;
+  const bool rank_bin = !take_bin && in_bin <= (uint32_t)kMaxCand;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  // keys above the bin (and the whole bin when all of it is kept) are marked;
+  // the bin's keys are gathered per wave with ballots for the ranking
+  uint32_t wrun = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const uint32_t k = kr[u];
-      if (k != 0 && (keep_all || k >= thr)) {
-        const int beta = slots.block_of(u * kThreads + tid);
-        atomicOr(&bitmap[beta >> 5], 1u << (beta & 31));
+  for (int u = 0; u < KPT; ++u) {
+    const uint32_t k = kr[u];
+    const int c = u * kThreads + tid;
+    const bool inb = k != 0 && k >= prefix && k <= pmax;
+    if (k > pmax || (take_bin && inb)) mark(bitmap, block_of(c));
+    if (rank_bin) {
+      const uint64_t m = __ballot(inb);
+      if (inb) {
+        const uint32_t pos = wrun + (uint32_t)__popcll(m & below);
+        sh.cand_key[wave][pos] = k;
+        sh.cand_slot[wave][pos] = c;
       }
+      wrun += (uint32_t)__popcll(m);
     }
-    keep_all = true;  // marked; skip the ranking below
   }
-  if (!keep_none && !keep_all) {
-    // rank of a tie = number of ties at smaller candidate indices: earlier
-    // slots, then earlier waves of the same slot, then lower lanes
+  if (rank_bin) {
+    if (lane == 0) sh.wcnt[wave] = wrun;
+    __syncthreads();
+    // rank of a bin key = bin keys before it in (key desc, candidate asc) order
+    uint32_t wc[kWaves], first = 0;
+    int w = -1;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      wc[w2] = sh.wcnt[w2];
+      if (w < 0 && (uint32_t)tid < first + wc[w2]) w = w2;
+      if (w < 0) first += wc[w2];
+    }
+    if (w >= 0) {
+      const uint32_t kt = sh.cand_key[w][tid - first];
+      const int ct = sh.cand_slot[w][tid - first];
+      uint32_t rank = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2)
+        for (uint32_t j = 0; j < wc[w2]; ++j) {
+          const uint32_t kj = sh.cand_key[w2][j];
+          const int cj = sh.cand_slot[w2][j];
+          rank += (kj > kt || (kj == kt && cj < ct)) ? 1u : 0u;
+        }
+      if (rank < remaining) mark(bitmap, block_of(ct));
+    }
+  } else if (!take_bin) {
+    // more than kMaxCand keys all equal to the threshold: the first
+    // `remaining` of them in candidate order are kept. Rank of a tie = ties
+    // at earlier slots, then at earlier waves of the same slot, then at lower
+    // lanes.
     uint64_t tie_mask[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      tie_mask[u] = __ballot(!keep_all && kr[u] != 0 && kr[u] == thr);
+      tie_mask[u] = __ballot(kr[u] != 0 && kr[u] == prefix);
       if (lane == 0) sh.tie_cnt[u][wave] = (uint32_t)__popcll(tie_mask[u]);
     }
     __syncthreads();
     uint32_t before = 0;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       uint32_t in_slot = 0, waves_before = 0;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const uint32_t cw = sh.tie_cnt[u][w];
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const uint32_t cw = sh.tie_cnt[u][w2];
         in_slot += cw;
-        waves_before += w < wave ? cw : 0u;
+        waves_before += w2 < wave ? cw : 0u;
       }
-      const uint32_t k = kr[u];
-      bool keep = k != 0 && (keep_all || k > thr);
-      if (!keep && k != 0 && k == thr)
-        keep = before + waves_before + (uint32_t)__popcll(tie_mask[u] & below) < ties_keep;
-      if (keep) {
-        const int beta = slots.block_of(u * kThreads + tid);
-        atomicOr(&bitmap[beta >> 5], 1u << (beta & 31));
-      }
+      if (kr[u] != 0 && kr[u] == prefix &&
+          before + waves_before + (uint32_t)__popcll(tie_mask[u] & below) < remaining)
+        mark(bitmap, block_of(u * kThreads + tid));
       before += in_slot;
     }
   }
-  emit_ids(p, unit, T, nb, bitmap, sh);
 }
 
-// Top-k + window + ascending ids for one unit, by the whole workgroup.
-__device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int T, const SlotMap& slots, int n,
-                            TopkShared& sh, uint32_t* dyn) {
+// Top-k of a unit with more candidates than the register path holds: keys in
+// LDS (`sk`, when lds_keys) or re-read from the published scores; full 11-bit
+// radix passes down to the exact threshold, ties ranked by a scan in
+// candidate order. Sets the kept blocks in `bitmap` (zeroed by the caller).
+__device__ __forceinline__ void topk_general(const SelectParams& p, int unit, const UnitGeom& ug,
+                                             TopkShared& sh, uint32_t* bitmap, uint32_t* sk,
+                                             bool lds_keys) {
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
-  const int nb = slots.nb;
-  const int words = (nb + 31) / 32;
-  uint32_t* bitmap = dyn;                          // p.out_blocks_max bits
-  uint32_t* sk = dyn + (p.out_blocks_max + 31) / 32;  // keys, when they fit
-  const bool lds_keys = p.n_slots_max <= kLdsKeys;  // matches the launch's LDS size
+  const int n = ug.n;
+  const SlotMap& slots = ug.slots;
   const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
-  for (int w = tid; w < words; w += kThreads) bitmap[w] = 0u;
 
   // 1. keys (0 = not a candidate), their number, largest and smallest key;
   //    the published scores are loaded in unrolled batches so they overlap
@@ -409,15 +685,15 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
     return slots.block_of(c) >= 0 ? order_key(published(&sc[c])) : 0u;
   };
   const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
-  const bool keep_none = k_eff == 0;
-  const bool keep_all = !keep_none && k_eff == n_valid;
+  if (k_eff == 0) return;
+  const bool keep_all = k_eff == n_valid;
 
   // 2. the k-th largest key `thr` and how many keys equal to it are kept
   uint32_t thr = 0, ties_keep = 0;
-  if (!keep_none && !keep_all && kmax == kmin) {
+  if (!keep_all && kmax == kmin) {
     thr = kmax;
     ties_keep = k_eff;
-  } else if (!keep_none && !keep_all) {
+  } else if (!keep_all) {
     const int common = __clz(kmax ^ kmin);  // < 32 here
     int shift = 32 - common;
     uint32_t prefix = common == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> common));
@@ -443,37 +719,102 @@ __device__ __forceinline__ void select_unit(const SelectParams& p, int unit, int
   }
 
   // 3. mark kept blocks; thread t scans candidates [t*per, (t+1)*per) in order
-  if (!keep_none) {
-    const int per = (n + kThreads - 1) / kThreads;
-    const int c0 = tid * per, c1 = min(c0 + per, n);
-    uint32_t ties = 0;
-    if (!keep_all)
-      for (int c = c0; c < c1; ++c) ties += key_of(c) == thr ? 1u : 0u;
-    uint32_t tot;
-    uint32_t rank = block_excl_scan(ties, &tot, sh);
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t k = key_of(c);
-      if (k == 0) continue;
-      bool keep = keep_all || k > thr;
-      if (!keep && k == thr) keep = rank++ < ties_keep;
-      if (keep) {
-        const int beta = slots.block_of(c);
-        atomicOr(&bitmap[beta >> 5], 1u << (beta & 31));
-      }
-    }
+  const int per = (n + kThreads - 1) / kThreads;
+  const int c0 = tid * per, c1 = min(c0 + per, n);
+  uint32_t ties = 0;
+  if (!keep_all)
+    for (int c = c0; c < c1; ++c) ties += key_of(c) == thr ? 1u : 0u;
+  uint32_t tot;
+  uint32_t rank = block_excl_scan(ties, &tot, sh);
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t k = key_of(c);
+    if (k == 0) continue;
+    bool keep = keep_all || k > thr;
+    if (!keep && k == thr) keep = rank++ < ties_keep;
+    if (keep) mark(bitmap, slots.block_of(c));
   }
-  emit_ids(p, unit, T, nb, bitmap, sh);
 }
 
-// TS: storage type of a summary element (float for mean rows, TE for boxes)
+// Window blocks into the bitmap, then the bitmap as ascending ids: to `list`
+// (LDS) and/or to `gids` / `*gcnt` (global), either may be null. Wave w
+// emits the bits of its quarter of the bitmap words, 64 bits per round (lane
+// l tests one bit, a ballot gives every set bit its position). Returns the
+// count in every thread; the list is complete when it returns.
+__device__ __forceinline__ int emit_ids(const SelectParams& p, const UnitGeom& ug, uint32_t* bitmap,
+                                        TopkShared& sh, int32_t* list, int32_t* gids,
+                                        int32_t* gcnt) {
+  const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
+  const int S = p.block_size, nb = ug.nb;
+  const int words = (nb + 31) / 32;
+  if (p.window > 0) {
+    const int64_t lo_tok = (int64_t)ug.T - p.window;
+    const int w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / S);
+    for (int beta = w0 + tid; beta < nb; beta += kThreads) mark(bitmap, beta);
+  }
+  __syncthreads();
+  const int wpw = (words + kWaves - 1) / kWaves;  // words of each wave
+  const int w_lo = wave * wpw, w_hi = min(w_lo + wpw, words);
+  uint32_t ones = 0;
+  for (int w = w_lo + lane; w < w_hi; w += kWave) ones += __popc(bitmap[w]);
+  ones = wave_sum_u(ones);
+  if (lane == 0) sh.wave_tot[wave] = ones;
+  __syncthreads();
+  uint32_t pos = 0, total = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    const uint32_t t = sh.wave_tot[w2];
+    pos += w2 < wave ? t : 0u;
+    total += t;
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  const uint32_t cap = (uint32_t)p.out_cap;
+  for (int w = w_lo; w < w_hi; w += 2) {  // wave-uniform
+    const int wl = w + (lane >> 5);
+    const bool set = wl < w_hi && ((bitmap[min(wl, w_hi - 1)] >> (lane & 31)) & 1u);
+    const uint64_t m = __ballot(set);
+    const uint32_t at = pos + (uint32_t)__popcll(m & below);
+    if (set && at < cap) {
+      const int id = wl * 32 + (lane & 31);
+      if (list) list[at] = id;
+      if (gids) gids[at] = id;
+    }
+    pos += (uint32_t)__popcll(m);
+  }
+  const int cnt = (int)min(total, cap);
+  if (gcnt && tid == 0) *gcnt = cnt;
+  __syncthreads();
+  return cnt;
+}
+
+// The whole selection of one unit by one workgroup, from the published
+// scores: top-k, window, ascending ids. ug = unit_geom(p, unit) (callers
+// compute it early so its loads overlap other work). dyn = dynamic LDS laid
+// out as [bitmap: out_blocks_max bits][keys: n_slots_max words, general path].
+__device__ __forceinline__ int select_from_scores(const SelectParams& p, int unit,
+                                                  const UnitGeom& ug, TopkShared& sh,
+                                                  uint32_t* dyn, int32_t* list, int32_t* gids,
+                                                  int32_t* gcnt) {
+  if (!p.gamma && ug.n <= kThreads * kRegKeys)
+    return topk_single(p, unit, ug, sh, list, gids, gcnt);
+  uint32_t* bitmap = dyn;
+  for (int w = thread_id(); w < (ug.nb + 31) / 32; w += kThreads) bitmap[w] = 0u;
+  if (ug.n <= kThreads * kRegKeys) {
+    topk_regs<true>(p, unit, ug, sh, bitmap);
+  } else {
+    __syncthreads();
+    uint32_t* sk = dyn + (p.out_blocks_max + 31) / 32;
+    topk_general(p, unit, ug, sh, bitmap, sk, p.n_slots_max <= kLdsKeys);
+  }
+  return emit_ids(p, ug, bitmap, sh, list, gids, gcnt);
+}
+
 // One scoring task: rows [chunk * kRowsPerWG, (chunk + 1) * kRowsPerWG) of
-// the unit's candidate slots, by the whole workgroup. Every task of the unit
-// (nchunks of them) arrives on the unit's counter; the last one to arrive
-// runs the top-k and returns true (in every thread), having written the
-// unit's ids and count with plain stores.
+// the unit's candidate slots, by the whole workgroup; their scores are
+// published (device-coherent stores) when it returns.
+// TS: storage type of a summary element (float for mean rows, TE for boxes).
 template <typename TE, int D, int KIND, int G>
-__device__ __forceinline__ bool select_task(const SelectParams& p, int unit, int chunk, int nchunks,
-                            TopkShared& sh, uint32_t* dyn) {
+__device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int chunk,
+                                            TopkShared& sh) {
   using TS = typename std::conditional<KIND == HS_SUMMARY_MEAN, float, TE>::type;
   constexpr int EPS = 16 / sizeof(TS);                        // elements per 16-byte load
   constexpr int ROW = (KIND == HS_SUMMARY_MEAN ? 1 : 2) * D;  // elements per row
@@ -482,12 +823,8 @@ __device__ __forceinline__ bool select_task(const SelectParams& p, int unit, int
   const KvView& kv = p.kv;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
-  const int T = clamp_len(kv, b);
-  int nb = (T + p.block_size - 1) / p.block_size;
-  nb = nb < p.out_blocks_max ? nb : p.out_blocks_max;
-  const SlotMap slots = make_slots(p, unit, nb);
-  int n_slots = p.gamma ? slots.gcnt * p.ratio : nb;
-  n_slots = n_slots < p.n_slots_max ? n_slots : p.n_slots_max;
+  const UnitGeom ug = unit_geom(p, unit);
+  const int n_slots = ug.n;
   const int c_begin = (chunk * kWaves + wave) * kRowsPerWave;
 
   static_assert(kRowsPerWG <= kThreads, "at most one staged score per thread");
@@ -519,7 +856,7 @@ __device__ __forceinline__ bool select_task(const SelectParams& p, int unit, int
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = cb + u * RPW + rg;
-        const int beta = c < c_end ? slots.block_of(c) : -1;
+        const int beta = c < c_end ? ug.slots.block_of(c) : -1;
         cs[u] = beta >= 0 ? c : -1;
         r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(
                                summ + (int64_t)beta * ROW * sizeof(TS) + li * 16)
@@ -537,25 +874,47 @@ __device__ __forceinline__ bool select_task(const SelectParams& p, int unit, int
       }
     }
   }
-  // publish the workgroup's scores with one coalesced store per thread
+  // publish the workgroup's scores with one coalesced store per thread, and
+  // the chunk's largest key and largest ~key (its key range for the top-k)
   __syncthreads();
-  {
-    const int c = chunk * kRowsPerWG + tid;
-    if (tid < kRowsPerWG && c < n_slots)
-      publish(&p.scores[(int64_t)unit * p.n_slots_max + c], sh.stage[tid]);
+  const int c = chunk * kRowsPerWG + tid;
+  const bool ok = tid < kRowsPerWG && c < n_slots && ug.slots.block_of(c) >= 0;
+  uint32_t kx = 0, ki = 0;
+  if (ok) {
+    const float v = sh.stage[tid];
+    publish(&p.scores[(int64_t)unit * p.n_slots_max + c], v);
+    kx = order_key(v);
+    ki = ~kx;
   }
-  // every workgroup of the unit arrives; the last one selects
-  if (!arrive_last(&p.counters[unit], nchunks, &sh.last)) return false;
-  if (n_slots <= kThreads * kRegKeys)
-    select_unit_regs<kRegKeys>(p, unit, T, slots, n_slots, sh, dyn);
-  else
-    select_unit(p, unit, T, slots, n_slots, sh, dyn);
-  return true;
+  kx = wave_max_u(kx);
+  ki = wave_max_u(ki);
+  if (lane == 0) {
+    sh.red[1][wave] = kx;
+    sh.red[2][wave] = ki;
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      kx = max(kx, sh.red[1][w]);
+      ki = max(ki, sh.red[2][w]);
+    }
+    uint32_t* ck = p.chunk_keys + ((int64_t)unit * select_chunks(p.n_slots_max) + chunk) * 2;
+    publish_i32(reinterpret_cast<int32_t*>(ck), (int32_t)kx);
+    publish_i32(reinterpret_cast<int32_t*>(ck + 1), (int32_t)ki);
+  }
 }
 
-// Number of scoring tasks of a unit for a level with n_slots_max candidates.
-__host__ __device__ inline int select_chunks(int n_slots_max) {
-  return (n_slots_max + kRowsPerWG - 1) / kRowsPerWG;
+// One task of the selection kernel: score a chunk, arrive on the unit's
+// counter (nchunks tasks); the last one to arrive selects and writes the
+// unit's ids and count to global memory.
+template <typename TE, int D, int KIND, int G>
+__device__ __forceinline__ void select_task(const SelectParams& p, int unit, int chunk, int nchunks,
+                                            TopkShared& sh, uint32_t* dyn) {
+  score_chunk<TE, D, KIND, G>(p, unit, chunk, sh);
+  if (!arrive_last(counter_of(p.counters, unit), nchunks, &sh.last)) return;
+  select_from_scores(p, unit, unit_geom(p, unit), sh, dyn, nullptr,
+                     p.out_ids + (int64_t)unit * p.out_cap, p.out_cnt + unit);
 }
 
 }  // namespace

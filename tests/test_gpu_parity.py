@@ -162,9 +162,10 @@ def test_fused_select_decode_equals_separate_calls(name):
         assert torch.equal(cnt_f, cnt_s), (name, call)
         assert torch.equal(ids_f, ids_s), (name, call)
         assert torch.equal(out_f, out_s), (name, call, float((out_f - out_s).abs().max()))
-    # the workspace starts with the selection's arrival counters (two levels)
+    # the workspace starts with the selection's arrival counters (two levels,
+    # one 256-byte line per unit)
     units_n = P.w.batch * P.w.hkv
-    assert int(ws[:8 * units_n].view(torch.int32).abs().sum()) == 0, name
+    assert int(ws[:2 * 256 * units_n].view(torch.int32).abs().sum()) == 0, name
     log("%s fused == separate, 3 calls" % name)
 
 
