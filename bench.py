@@ -7,12 +7,11 @@ Quest min/max summaries over 32-token blocks, top-128 blocks + 512-token
 window, selection shared by the 4 query heads of a KV group). Inputs are
 seeded synthetic data (synth/), resident in HBM before timing starts.
 
-One step = the whole decode-time path through the C ABI:
-  1. hs_build_summaries from the last block on (refresh of the growing block),
-  2. hs_select_decode: selection (score all 4096 blocks per unit, top-k,
-     window union) and exact softmax attention over the selected blocks, in
-     one launch (--path separate: hs_select_blocks then hs_sparse_decode,
-     same results).
+One step = the whole decode-time path through the C ABI, hs_decode_step in
+one launch: refresh of the growing last block's summary, selection (score
+all 4096 blocks per unit, top-k, window union) and exact softmax attention
+over the selected blocks (--path separate: hs_build_summaries,
+hs_select_blocks, hs_sparse_decode as three launches, same results).
 
 The per-step working set (summaries + selected KV, ~143 MB) would fit in the
 256 MiB Infinity Cache, so the timed loop rotates over `--copies` identical
@@ -72,8 +71,8 @@ _CSRC = "hierarchical_sparse_attention_amd/csrc/"
 KERNEL_SOURCES = {
     "hs_sparse_decode": [_CSRC + f for f in ("decode.hip", "decode_impl.h", "hs_internal.h")],
     "hs_select_blocks": [_CSRC + f for f in ("select.hip", "select_impl.h", "hs_internal.h")],
-    "hs_select_decode": [_CSRC + f for f in ("step.hip", "select_impl.h", "decode_impl.h",
-                                             "hs_internal.h")],
+    "hs_decode_step": [_CSRC + f for f in ("step.hip", "select_impl.h", "decode_impl.h",
+                                           "summ_impl.h", "hs_internal.h")],
 }
 
 
@@ -174,7 +173,7 @@ def main():
 
     last_block = (w.T - 1) // w.S
     names = ["hs_build_summaries(last block)", "hs_select_blocks", "hs_sparse_decode",
-             "hs_select_decode"]
+             "hs_select_decode", "hs_decode_step"]
     for c in copies:
         c["calls"] = [
             hs.prepare_build_summaries(c["kv"], c["fine"], last_block, stream),
@@ -184,8 +183,10 @@ def main():
                                      c["ws_d"], stream),
             hs.prepare_select_decode(c["kv"], c["q"], c["fine"], w.top_k, w.window, c["ids"],
                                      c["cnt"], c["out"], c["ws_f"], stream),
+            hs.prepare_decode_step(c["kv"], c["q"], c["fine"], w.top_k, w.window, last_block,
+                                   c["ids"], c["cnt"], c["out"], c["ws_f"], stream),
         ]
-    step_calls = [0, 3] if args.path == "fused" else [0, 1, 2]
+    step_calls = [4] if args.path == "fused" else [0, 1, 2]
 
     def step(c):
         for j in step_calls:
@@ -219,7 +220,7 @@ def main():
         call_ms.append(float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(copies))
         del g
     call_ms = np.array(call_ms)
-    log("per-call mean ms: refresh %.4f select %.4f decode %.4f select+decode %.4f" %
+    log("per-call mean ms: refresh %.4f select %.4f decode %.4f select+decode %.4f step %.4f" %
         tuple(call_ms))
 
     # ---------------------------------------------------------- graphs
@@ -285,9 +286,9 @@ def main():
 
     dec_ms = float(call_ms[2])
     sel_ms = float(call_ms[1])
-    fused_ms = float(call_ms[3])
+    step_ms = float(call_ms[4])
     if args.path == "fused":
-        dominant, dom_bytes, dom_ms = "hs_select_decode", bytes_select + bytes_decode, fused_ms
+        dominant, dom_bytes, dom_ms = "hs_decode_step", bytes_step, step_ms
     elif bytes_decode >= bytes_select:
         dominant, dom_bytes, dom_ms = "hs_sparse_decode", bytes_decode, dec_ms
     else:

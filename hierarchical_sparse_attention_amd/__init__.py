@@ -27,7 +27,7 @@ KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 # Names declared in include/hs_attn.h; the CPU tests check that each is exported.
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
-           "hs_select_decode", "hs_status_string", "hs_version")
+           "hs_select_decode", "hs_decode_step", "hs_status_string", "hs_version")
 
 
 class HsError(RuntimeError):
@@ -82,9 +82,11 @@ def lib() -> ctypes.CDLL:
         L.hs_select_decode.argtypes = [P(hs_select_params), P(hs_kv_cache), vp,
                                        P(hs_summaries), P(hs_summaries), ctypes.c_float, vp, vp,
                                        vp, vp, sz, vp]
+        L.hs_decode_step.argtypes = [P(hs_select_params), P(hs_kv_cache), vp, P(hs_summaries),
+                                     P(hs_summaries), i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
-                     "hs_select_decode_workspace_size", "hs_select_decode"):
+                     "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -289,6 +291,25 @@ def hs_select_decode(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, 
     _check("hs_select_decode", lib().hs_select_decode(*args))
 
 
+def _decode_step_args(kv, q, fine, top_k, window, refresh_begin, block_ids, num_selected, out,
+                      workspace, coarse, top_k_coarse, scale, stream):
+    args, keep = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
+                                     workspace, coarse, top_k_coarse, scale, stream)
+    return args[:5] + (int(refresh_begin),) + args[5:], keep
+
+
+def hs_decode_step(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                   refresh_begin: int, block_ids: torch.Tensor, num_selected: torch.Tensor,
+                   out: torch.Tensor, workspace: torch.Tensor, coarse: Optional[Summaries] = None,
+                   top_k_coarse: int = 0, scale: float = 0.0, stream=None) -> None:
+    """hs_build_summaries from refresh_begin on (each level), then
+    hs_select_decode, in one launch for a single level; the workspace is
+    that of hs_select_decode."""
+    args, _ = _decode_step_args(kv, q, fine, top_k, window, refresh_begin, block_ids,
+                                num_selected, out, workspace, coarse, top_k_coarse, scale, stream)
+    _check("hs_decode_step", lib().hs_decode_step(*args))
+
+
 def hs_version() -> int:
     return lib().hs_version()
 
@@ -353,3 +374,14 @@ def prepare_select_decode(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: 
     args, keep = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
                                      workspace, coarse, top_k_coarse, scale, stream)
     return Prepared("hs_select_decode", lib().hs_select_decode, args, keep)
+
+
+def prepare_decode_step(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
+                        refresh_begin: int, block_ids: torch.Tensor, num_selected: torch.Tensor,
+                        out: torch.Tensor, workspace: torch.Tensor, stream,
+                        coarse: Optional[Summaries] = None, top_k_coarse: int = 0,
+                        scale: float = 0.0) -> Prepared:
+    args, keep = _decode_step_args(kv, q, fine, top_k, window, refresh_begin, block_ids,
+                                   num_selected, out, workspace, coarse, top_k_coarse, scale,
+                                   stream)
+    return Prepared("hs_decode_step", lib().hs_decode_step, args, keep)

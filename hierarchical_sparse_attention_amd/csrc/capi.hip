@@ -220,6 +220,7 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
     sp.out_cap = (int32_t)L.kc_cap;
     sp.out_blocks_max = (int32_t)L.nc;
     sp.counters = counters + L.units * hs::kCounterStride;
+    sp.refresh_begin = -1;
     const hipError_t e = hs::launch_select(sp, s);
     if (e != hipSuccess) return from_hip(e);
   }
@@ -241,6 +242,7 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
   sp.out_cap = prm->max_selected;
   sp.out_blocks_max = (int32_t)L.nb_fine;
   sp.counters = counters;
+  sp.refresh_begin = -1;
   *out = sp;
   return HS_OK;
 }
@@ -363,27 +365,46 @@ hs_status hs_select_decode_workspace_size(const hs_select_params* p, const hs_kv
   return st;
 }
 
-hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
-                           const hs_summaries* fine, const hs_summaries* coarse, float scale,
-                           int32_t* block_ids, int32_t* num_selected, float* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// hs_select_decode and hs_decode_step; refresh_begin < 0: no refresh.
+hs_status select_decode(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                        const hs_summaries* fine, const hs_summaries* coarse, int32_t refresh_begin,
+                        float scale, int32_t* block_ids, int32_t* num_selected, float* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t s) {
   StepLayout L;
   hs_status st = check_step(prm, kv, fine, coarse, &L);
   if (st != HS_OK) return st;
   if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
   if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (refresh_begin >= 0 && L.sel.two_level) {
+    // two levels: both tables are refreshed by the summary kernel first
+    hs_status r = hs_build_summaries(kv, refresh_begin, fine, s);
+    if (r != HS_OK) return r;
+    const int32_t cb = (int32_t)((int64_t)refresh_begin * fine->block_size / coarse->block_size);
+    r = hs_build_summaries(kv, cb, coarse, s);
+    if (r != HS_OK) return r;
+    refresh_begin = -1;
+  }
   hs::StepParams p;
   st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected, ws + L.off_sel, L.sel, s,
                      &p.sel);
   if (st != HS_OK) return st;
   p.dec = decode_params(kv, q, scale, fine->block_size, block_ids, num_selected,
                         prm->max_selected, out, ws + L.off_dec, L.dec);
+  p.sel.refresh_begin = refresh_begin;
   if (!hs::step_fits(p.sel.out_blocks_max, p.sel.n_slots_max, p.sel.out_cap)) {
-    // id lists too long for the fused kernel's LDS: the two stages as two
+    // id lists too long for the fused kernel's LDS: the stages as separate
     // launches, with the same results
+    if (refresh_begin >= 0) {
+      const hs_status r = hs_build_summaries(kv, refresh_begin, fine, s);
+      if (r != HS_OK) return r;
+      p.sel.refresh_begin = -1;
+    }
     const hipError_t e = hs::launch_select(p.sel, s);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(hs::launch_decode(p.dec, s));
@@ -394,6 +415,29 @@ hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, c
   p.total = p.units * (p.n_chunks + p.dec.n_splits);
   p.list_cap = p.sel.out_cap;
   return from_hip(hs::launch_step(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                           const hs_summaries* fine, const hs_summaries* coarse, float scale,
+                           int32_t* block_ids, int32_t* num_selected, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return select_decode(prm, kv, q, fine, coarse, -1, scale, block_ids, num_selected, out,
+                       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+hs_status hs_decode_step(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
+                         const hs_summaries* fine, const hs_summaries* coarse,
+                         int32_t refresh_begin, float scale, int32_t* block_ids,
+                         int32_t* num_selected, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (refresh_begin < 0) return HS_ERR_INVALID_ARG;
+  if (kv && (!kv->k_pool || !aligned16(kv->k_pool))) return HS_ERR_INVALID_ARG;
+  return select_decode(prm, kv, q, fine, coarse, refresh_begin, scale, block_ids, num_selected,
+                       out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -200,6 +200,7 @@ struct SelectParams {
   int32_t out_cap;
   int32_t out_blocks_max;    // blocks of this level per unit (bitmap bits)
   int32_t* counters;         // [units] workgroup arrivals; zero between calls
+  int32_t refresh_begin;     // >= 0: rebuild blocks from here on before scoring (single level)
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 // Dynamic LDS of a selection workgroup: bitmap words, then keys (general path).

@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "hs_internal.h"
+#include "summ_impl.h"
 
 namespace hs {
 namespace {
@@ -810,7 +811,11 @@ __device__ __forceinline__ int select_from_scores(const SelectParams& p, int uni
 
 // One scoring task: rows [chunk * kRowsPerWG, (chunk + 1) * kRowsPerWG) of
 // the unit's candidate slots, by the whole workgroup; their scores are
-// published (device-coherent stores) when it returns.
+// published (device-coherent stores) when it returns. With
+// p.refresh_begin >= 0 (single level) the chunk's blocks at or beyond it are
+// first rebuilt from the K cache and stored (the per-step refresh of the
+// growing block), then scored from the stored rows with the same arithmetic
+// as every other row.
 // TS: storage type of a summary element (float for mean rows, TE for boxes).
 template <typename TE, int D, int KIND, int G>
 __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int chunk,
@@ -820,20 +825,23 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   constexpr int ROW = (KIND == HS_SUMMARY_MEAN ? 1 : 2) * D;  // elements per row
   constexpr int LPR = ROW / EPS;                              // lanes per row
   constexpr int RPW = kWave / LPR;                            // rows per wave instruction
+  constexpr int64_t kRowBytes = ROW * sizeof(TS);
   const KvView& kv = p.kv;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
   const UnitGeom ug = unit_geom(p, unit);
   const int n_slots = ug.n;
-  const int c_begin = (chunk * kWaves + wave) * kRowsPerWave;
-
+  const int c_wg = chunk * kRowsPerWG;  // first slot of the workgroup
+  const int c_begin = c_wg + wave * kRowsPerWave;
+  const int li = lane % LPR, rg = lane / LPR;
   static_assert(kRowsPerWG <= kThreads, "at most one staged score per thread");
-  if (c_begin < n_slots) {  // wave-uniform
-    const int li = lane % LPR, rg = lane / LPR;
-    const int e0 = li * EPS;                                 // first element of the lane
-    const int part = KIND == HS_SUMMARY_MEAN ? 0 : e0 / D;   // 0: min (or mean), 1: max
+
+  // the unit's G query heads folded into per-element coefficients
+  float coef[EPS];
+  {
+    const int e0 = li * EPS;                                // first element of the lane
+    const int part = KIND == HS_SUMMARY_MEAN ? 0 : e0 / D;  // 0: min (or mean), 1: max
     const int dim0 = e0 % D;
-    float coef[EPS];
 #pragma unroll
     for (int k = 0; k < EPS; ++k) {
       float c = 0.f;
@@ -846,10 +854,20 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       }
       coef[k] = c;
     }
-    const uint8_t* summ = reinterpret_cast<const uint8_t*>(p.summ) +
-                          (int64_t)unit * p.max_blocks * ROW * sizeof(TS);
+  }
+  // score of one row from the 16 bytes each of its LPR lanes holds
+  auto row_score = [&](const uint4& r) {
+    float f[EPS];
+    Vec16<TS>::unpack(r, f);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < EPS; ++k) acc = fmaf(coef[k], f[k], acc);
+    return group_sum<LPR>(acc);
+  };
+  const uint8_t* summ = reinterpret_cast<const uint8_t*>(p.summ) +
+                        (int64_t)unit * p.max_blocks * kRowBytes;
+  if (c_begin < n_slots) {  // wave-uniform
     const int c_end = min(c_begin + kRowsPerWave, n_slots);
-    const int c_wg = chunk * kRowsPerWG;  // first slot of the workgroup
     for (int cb = c_begin; cb < c_end; cb += RPW * kUnroll) {
       uint4 r[kUnroll];
       int cs[kUnroll];
@@ -858,26 +876,38 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
         const int c = cb + u * RPW + rg;
         const int beta = c < c_end ? ug.slots.block_of(c) : -1;
         cs[u] = beta >= 0 ? c : -1;
-        r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(
-                               summ + (int64_t)beta * ROW * sizeof(TS) + li * 16)
+        r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
                          : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        float f[EPS];
-        Vec16<TS>::unpack(r[u], f);
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < EPS; ++k) acc = fmaf(coef[k], f[k], acc);
-        acc = group_sum<LPR>(acc);
+        const float acc = row_score(r[u]);
         if (li == 0 && cs[u] >= 0) sh.stage[cs[u] - c_wg] = acc;
       }
+    }
+  }
+  // refresh: rebuild this chunk's blocks in [refresh_begin, n) from K
+  const int r0 = max(p.refresh_begin, c_wg), r1 = min(n_slots, c_wg + kRowsPerWG);
+  if (p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1) {  // uniform
+    for (int beta = r0 + wave; beta < r1; beta += kWaves)
+      summarize_block<TE, D, KIND>(kv, const_cast<void*>(p.summ),
+                                   (int64_t)unit * p.max_blocks + beta, b, g, beta,
+                                   p.block_size, ug.T);
+    __builtin_amdgcn_s_waitcnt(0);  // rebuilt rows are stored
+    __syncthreads();                // (and the stale scores of those rows staged)
+    for (int cb = r0 + wave * RPW; cb < r1; cb += kWaves * RPW) {  // wave-uniform
+      const int c = min(cb + rg, r1 - 1);
+      const int32_t* w = reinterpret_cast<const int32_t*>(summ + c * kRowBytes + li * 16);
+      const uint4 r = make_uint4(published_i32(w), published_i32(w + 1), published_i32(w + 2),
+                                 published_i32(w + 3));
+      const float acc = row_score(r);
+      if (li == 0 && cb + rg < r1) sh.stage[cb + rg - c_wg] = acc;
     }
   }
   // publish the workgroup's scores with one coalesced store per thread, and
   // the chunk's largest key and largest ~key (its key range for the top-k)
   __syncthreads();
-  const int c = chunk * kRowsPerWG + tid;
+  const int c = c_wg + tid;
   const bool ok = tid < kRowsPerWG && c < n_slots && ug.slots.block_of(c) >= 0;
   uint32_t kx = 0, ki = 0;
   if (ok) {

@@ -14,7 +14,9 @@
  *                       read in place from a paged KV cache
  *
  * hs_select_decode runs the last two stages for one layer in a single launch
- * (same results as hs_select_blocks followed by hs_sparse_decode).
+ * (same results as hs_select_blocks followed by hs_sparse_decode), and
+ * hs_decode_step all three as one decode step: the refresh of the trailing
+ * summary blocks, the selection and the attention.
  *
  * Sources (web pages; cited by title and section):
  *   [QSA]     "8x256K long-context sparse attention: porting HiSparse to QSA"
@@ -248,9 +250,9 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
  * selection is done, while other units are still being scored.
  * workspace: device buffer of at least hs_select_decode_workspace_size()
  *   bytes, 16-byte aligned and ZERO-FILLED before its first use; it holds
- *   the workspaces of both stages plus per-unit ready flags. Every call returns counters and flags to zero, so it can be
- *   reused by later calls on the same stream but must not be shared by calls
- *   that may run at the same time. */
+ *   the workspaces of both stages. Every call returns its counters to zero,
+ *   so it can be reused by later calls on the same stream but must not be
+ *   shared by calls that may run at the same time. */
 hs_status hs_select_decode_workspace_size(const hs_select_params* p,
                                           const hs_kv_cache* kv,
                                           const hs_summaries* fine,
@@ -262,6 +264,27 @@ hs_status hs_select_decode(const hs_select_params* p, const hs_kv_cache* kv,
                            int32_t* block_ids, int32_t* num_selected,
                            float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* One decode step of one layer ([SGL 2.2] decode phase after a token is
+ * appended; [HiSp 3.1] the per-block table is updated as the cache is
+ * written; [QSA 3.2], [QSA 3.3]): the summary blocks
+ * [refresh_begin, ceil(T_b / S)) of `fine` (and, with two levels, the
+ * coarse blocks from refresh_begin * S / C on) are rebuilt from the K cache
+ * as hs_build_summaries would, then the selection and the attention of
+ * hs_select_decode run on the refreshed tables. Results (the tables, ids,
+ * counts and outputs) are bitwise identical to hs_build_summaries on each
+ * table followed by hs_select_decode.
+ *   refresh_begin : >= 0; ceil(T_b / S) - 1 refreshes only the growing last
+ *                   block; a value at or past every unit's block count
+ *                   refreshes nothing. Negative values are rejected.
+ * Requires kv->k_pool. The workspace is that of hs_select_decode
+ * (hs_select_decode_workspace_size), with the same rules. */
+hs_status hs_decode_step(const hs_select_params* p, const hs_kv_cache* kv,
+                         const void* q, const hs_summaries* fine,
+                         const hs_summaries* coarse, int32_t refresh_begin,
+                         float scale, int32_t* block_ids,
+                         int32_t* num_selected, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* hs_status_string(hs_status s);

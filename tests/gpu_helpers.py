@@ -106,6 +106,24 @@ class Problem:
         hs.hs_select_decode(kv, q, summ["fine"], k, W, ids, cnt, out, ws, coarse, w.top_k_coarse)
         return ids, cnt, out, ws
 
+    def decode_step(self, q: torch.Tensor, summ: Dict[str, hs.Summaries], refresh_begin: int,
+                    layer=0, ws=None):
+        """hs_decode_step (refresh + selection + attention); returns ids,
+        counts, out and the workspace."""
+        w, kv = self.w, self.kvs[layer]
+        cap = min(w.nb, min(w.top_k, w.nb) + -(-w.window // w.S) + 1)  # as select_decode
+        ids = torch.full((w.batch, w.hkv, cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+        coarse = summ.get("coarse")
+        if ws is None:
+            n = hs.hs_select_decode_workspace_size(kv, summ["fine"], w.hq, w.top_k, w.window, cap,
+                                                   coarse, w.top_k_coarse)
+            ws = hs.workspace(n, "cuda")
+        hs.hs_decode_step(kv, q, summ["fine"], w.top_k, w.window, refresh_begin, ids, cnt, out,
+                          ws, coarse, w.top_k_coarse)
+        return ids, cnt, out, ws
+
     def decode(self, q: torch.Tensor, ids: torch.Tensor, cnt: torch.Tensor, layer=0,
                block_size=None):
         w, kv = self.w, self.kvs[layer]

@@ -169,6 +169,48 @@ def test_fused_select_decode_equals_separate_calls(name):
     log("%s fused == separate, 3 calls" % name)
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("where", ["last", "many"])
+def test_decode_step_equals_refresh_then_select_decode(name, where):
+    """hs_decode_step (summary refresh from refresh_begin on, selection and
+    attention in one call) leaves the same summary tables, ids and counts
+    and bitwise the same outputs as hs_build_summaries from refresh_begin
+    (each level) followed by hs_select_decode. The refreshed rows start out
+    poisoned in both tables; "many" refreshes 300 blocks (several scoring
+    chunks of the fused launch)."""
+    P = problem(name)
+    w = P.w
+    kv = P.kvs[0]
+    q = P.q()
+    refresh_begin = w.nb - 1 if where == "last" else max(0, w.nb - 300)
+    tables = []
+    for _ in range(2):
+        summ = P.summaries()
+        summ["fine"].data[:, :, refresh_begin:] = 7.0
+        if "coarse" in summ:
+            cb = refresh_begin * w.S // w.coarse_S
+            summ["coarse"].data[:, :, cb:] = 7.0
+        tables.append(summ)
+    ref, got = tables
+    hs.hs_build_summaries(kv, ref["fine"], refresh_begin)
+    if "coarse" in ref:
+        hs.hs_build_summaries(kv, ref["coarse"], refresh_begin * w.S // w.coarse_S)
+    ids_r, cnt_r, out_r, _ = P.select_decode(q, ref)
+    ws = None
+    for call in range(2):  # the second call on the same workspace repeats the first
+        ids_g, cnt_g, out_g, ws = P.decode_step(q, got, refresh_begin, ws=ws)
+        torch.cuda.synchronize()
+        for lvl in ref:  # rows past a unit's block count are never written
+            S = ref[lvl].block_size
+            for b, T in enumerate(w.seq_lens_array()):
+                nb_b = -(-int(T) // S)
+                assert torch.equal(ref[lvl].data[b, :, :nb_b], got[lvl].data[b, :, :nb_b]), (
+                    name, where, lvl, call, b)
+        assert torch.equal(cnt_g, cnt_r) and torch.equal(ids_g, ids_r), (name, where, call)
+        assert torch.equal(out_g, out_r), (name, where, call)
+    log("%s decode step (refresh from %d) == refresh + select_decode" % (name, refresh_begin))
+
+
 @pytest.mark.parametrize("top_k,window", [(0, 256), (0, 0), (10 ** 6, 0), (3, 10 ** 6), (64, 1)])
 def test_selection_edge_values(top_k, window):
     """k = 0 (window only), nothing selected at all, k >= number of blocks
