@@ -855,15 +855,31 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       coef[k] = c;
     }
   }
-  // score of one row from the 16 bytes each of its LPR lanes holds
-  auto row_score = [&](const uint4& r) {
-    float f[EPS];
-    Vec16<TS>::unpack(r, f);
+  // score of one row from the EPS elements each of its LPR lanes holds
+  auto row_dot = [&](const float (&f)[EPS]) {
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < EPS; ++k) acc = fmaf(coef[k], f[k], acc);
     return group_sum<LPR>(acc);
   };
+  auto row_score = [&](const uint4& r) {
+    float f[EPS];
+    Vec16<TS>::unpack(r, f);
+    return row_dot(f);
+  };
+  // Refresh of this chunk's blocks in [refresh_begin, n): when each such
+  // block has a wave of its own and few enough tokens, the wave issues the
+  // block's K loads before the streaming loop below and rebuilds, stores and
+  // scores the row (from registers, with the stored values) after it.
+  constexpr int kRefreshLoads = 16;
+  constexpr int kTPW = kWave / (D / Vec16<TE>::EPL);  // tokens per K load instruction
+  const int r0 = max(p.refresh_begin, c_wg), r1 = min(n_slots, c_wg + kRowsPerWG);
+  const bool refresh = p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1;  // uniform
+  const bool early = refresh && r1 - r0 <= kWaves && p.block_size <= kRefreshLoads * kTPW;
+  const int my_row = r0 + wave;
+  uint4 rk[kRefreshLoads];
+  uint32_t rk_ok = 0;
+  if (early && my_row < r1) rk_ok = summ_load<TE, D, kRefreshLoads>(kv, b, g, my_row, p.block_size, ug.T, rk);
   const uint8_t* summ = reinterpret_cast<const uint8_t*>(p.summ) +
                         (int64_t)unit * p.max_blocks * kRowBytes;
   if (c_begin < n_slots) {  // wave-uniform
@@ -886,9 +902,22 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       }
     }
   }
-  // refresh: rebuild this chunk's blocks in [refresh_begin, n) from K
-  const int r0 = max(p.refresh_begin, c_wg), r1 = min(n_slots, c_wg + kRowsPerWG);
-  if (p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1) {  // uniform
+  if (early) {
+    __syncthreads();  // the stale scores of the refreshed rows are staged
+    if (my_row < r1) {
+      float a0[Vec16<TE>::EPL], a1[Vec16<TE>::EPL];
+      summ_reduce<TE, D, KIND, kRefreshLoads>(rk, rk_ok, a0, a1);
+      const int n_tok = min(my_row * p.block_size + p.block_size, ug.T) - my_row * p.block_size;
+      summ_store<TE, D, KIND>(const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + my_row,
+                              a0, a1, n_tok);
+      float f[EPS];
+      summ_row_elems<TE, D, KIND, EPS>(a0, a1, n_tok, f);
+      const float acc = row_dot(f);
+      if (lane == 0) sh.stage[my_row - c_wg] = acc;
+    }
+  } else if (refresh) {
+    // more blocks than waves, or long blocks: rebuild, store, and score the
+    // stored rows (device-coherent loads)
     for (int beta = r0 + wave; beta < r1; beta += kWaves)
       summarize_block<TE, D, KIND>(kv, const_cast<void*>(p.summ),
                                    (int64_t)unit * p.max_blocks + beta, b, g, beta,

@@ -20,6 +20,33 @@ namespace {
 
 constexpr int kSummUnroll = 8;
 
+// 16 bytes at byte `col` of the rows of tokens t_u = first + u * step
+// (u < N) of unit (b, g) in `pool`, for the tokens below t_end whose page is
+// valid (ok[u]); the others read row 0 of page 0 instead (in bounds, ignored).
+// All page-table loads are issued first and every row load after them, with
+// no branch on loaded values, so the N round trips overlap.
+template <int N>
+__device__ __forceinline__ void load_rows(const KvView& kv, const uint8_t* pool, int b, int g,
+                                          int first, int step, int t_end, int col,
+                                          uint4 (&r)[N], bool (&ok)[N]) {
+  int page[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int t = min(first + u * step, max(t_end - 1, 0));
+    page[u] = kv.page_table[(int64_t)b * kv.max_pages + t / kv.page_size];
+  }
+  const int64_t row_bytes = (int64_t)kv.head_dim * kv.elem_bytes;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int t = first + u * step;
+    ok[u] = t < t_end && (unsigned)page[u] < (unsigned)kv.num_phys_pages;
+    const int64_t off = ok[u] ? (((int64_t)page[u] * kv.num_kv_heads + g) * kv.page_size +
+                                 t % kv.page_size) * row_bytes
+                              : 0;
+    r[u] = *reinterpret_cast<const uint4*>(pool + off + col);
+  }
+}
+
 // Summary row of block beta (tokens [beta S, min(beta S + S, T))) of unit
 // (b, g), by the calling wave, stored at row `row` of `out` (mean: float32
 // [max_blocks][D] per unit; min/max: TE [max_blocks][2][D]).
@@ -42,14 +69,7 @@ __device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int
   for (int base = t0 + tg; base < t1; base += TPW * kSummUnroll) {
     uint4 r[kSummUnroll];
     bool ok[kSummUnroll];
-#pragma unroll
-    for (int u = 0; u < kSummUnroll; ++u) {
-      const int t = base + u * TPW;
-      const int64_t off = t < t1 ? row_offset(kv, b, g, t) : -1;
-      ok[u] = off >= 0;
-      r[u] = ok[u] ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
-                   : make_uint4(0, 0, 0, 0);
-    }
+    load_rows<kSummUnroll>(kv, kv.k_pool, b, g, base, TPW, t1, li * 16, r, ok);
 #pragma unroll
     for (int u = 0; u < kSummUnroll; ++u) {
       if (!ok[u]) continue;
@@ -109,6 +129,144 @@ __device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int
     uint8_t* o = reinterpret_cast<uint8_t*>(out) + row * 2 * D * (int64_t)sizeof(TE);
     *reinterpret_cast<uint4*>(o + li * 16) = lo;
     *reinterpret_cast<uint4*>(o + D * sizeof(TE) + li * 16) = hi;
+  }
+}
+
+// The same summary as summarize_block for a block of at most NL * TPW
+// tokens, in two steps so that the loads can be issued early and used later:
+// summ_load issues the block's K rows (NL 16-byte loads per lane, in the
+// token order of summarize_block), summ_reduce folds them (every lane ends
+// with the block's combined values for its dims, as in summarize_block before
+// its store). Sums run in the same per-lane token order, so the results are
+// bitwise those of summarize_block.
+template <typename TE, int D, int NL>
+__device__ __forceinline__ uint32_t summ_load(const KvView& kv, int b, int g, int beta, int S,
+                                              int T, uint4 (&r)[NL]) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = kWave / LPT;
+  const int lane = thread_id() & (kWave - 1);
+  const int tg = lane / LPT, li = lane % LPT;
+  const int t0 = beta * S, t1 = min(t0 + S, T);
+  bool okb[NL];
+  load_rows<NL>(kv, kv.k_pool, b, g, t0 + tg, TPW, t1, li * 16, r, okb);
+  uint32_t ok = 0;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) ok |= (okb[u] ? 1u : 0u) << u;
+  return ok;
+}
+
+template <typename TE, int D, int KIND, int NL>
+__device__ __forceinline__ void summ_reduce(const uint4 (&r)[NL], uint32_t ok,
+                                            float (&acc0)[Vec16<TE>::EPL],
+                                            float (&acc1)[Vec16<TE>::EPL]) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int LPT = D / EPL;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    acc0[k] = KIND == HS_SUMMARY_MEAN ? 0.f : INFINITY;
+    acc1[k] = -INFINITY;
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    if (!((ok >> u) & 1u)) continue;
+    float f[EPL];
+    Vec16<TE>::unpack(r[u], f);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      if (KIND == HS_SUMMARY_MEAN) {
+        acc0[k] += f[k];
+      } else {
+        acc0[k] = fminf(acc0[k], f[k]);
+        acc1[k] = fmaxf(acc1[k], f[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = LPT; s < kWave; s *= 2) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      const float o0 = __shfl_xor(acc0[k], s);
+      if (KIND == HS_SUMMARY_MEAN) {
+        acc0[k] += o0;
+      } else {
+        const float o1 = __shfl_xor(acc1[k], s);
+        acc0[k] = fminf(acc0[k], o0);
+        acc1[k] = fmaxf(acc1[k], o1);
+      }
+    }
+  }
+}
+
+// Store of a reduced summary row (acc from summ_reduce; n valid tokens), as
+// summarize_block stores it.
+template <typename TE, int D, int KIND>
+__device__ __forceinline__ void summ_store(void* out, int64_t row,
+                                           const float (&acc0)[Vec16<TE>::EPL],
+                                           const float (&acc1)[Vec16<TE>::EPL], int n_tok) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int LPT = D / EPL;
+  const int lane = thread_id() & (kWave - 1);
+  const int tg = lane / LPT, li = lane % LPT;
+  if (tg != 0) return;
+  if (KIND == HS_SUMMARY_MEAN) {
+    const float n = (float)n_tok;
+    float* o = reinterpret_cast<float*>(out) + row * D + li * EPL;
+#pragma unroll
+    for (int k = 0; k < EPL; k += 4)
+      *reinterpret_cast<float4*>(o + k) =
+          make_float4(acc0[k] / n, acc0[k + 1] / n, acc0[k + 2] / n, acc0[k + 3] / n);
+  } else {
+    uint4 lo, hi;
+    if constexpr (EPL == 4) {
+      lo = make_uint4(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]),
+                      __float_as_uint(acc0[2]), __float_as_uint(acc0[3]));
+      hi = make_uint4(__float_as_uint(acc1[0]), __float_as_uint(acc1[1]),
+                      __float_as_uint(acc1[2]), __float_as_uint(acc1[3]));
+    } else {
+      auto pack = [](float a, float c) {
+        return (__float_as_uint(a) >> 16) | (__float_as_uint(c) & 0xFFFF0000u);
+      };
+      lo = make_uint4(pack(acc0[0], acc0[1]), pack(acc0[2], acc0[3]), pack(acc0[4], acc0[5]),
+                      pack(acc0[6], acc0[7]));
+      hi = make_uint4(pack(acc1[0], acc1[1]), pack(acc1[2], acc1[3]), pack(acc1[4], acc1[5]),
+                      pack(acc1[6], acc1[7]));
+    }
+    uint8_t* o = reinterpret_cast<uint8_t*>(out) + row * 2 * D * (int64_t)sizeof(TE);
+    *reinterpret_cast<uint4*>(o + li * 16) = lo;
+    *reinterpret_cast<uint4*>(o + D * sizeof(TE) + li * 16) = hi;
+  }
+}
+
+// The EPS stored values that the scoring layout puts in this lane (elements
+// [li EPS, li EPS + EPS) of the row, li = lane % LPR), from a reduced
+// summary: the values summ_store writes, read from registers. Min/max rows
+// (and mean rows of float32 caches) hold a lane's elements in the lane
+// itself; mean rows of bfloat16 caches take half of another lane's 8 dims.
+template <typename TE, int D, int KIND, int EPS>
+__device__ __forceinline__ void summ_row_elems(const float (&acc0)[Vec16<TE>::EPL],
+                                               const float (&acc1)[Vec16<TE>::EPL], int n_tok,
+                                               float (&f)[EPS]) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int ROW = (KIND == HS_SUMMARY_MEAN ? 1 : 2) * D;
+  constexpr int LPR = ROW / EPS;
+  const int lane = thread_id() & (kWave - 1);
+  const int e0 = (lane % LPR) * EPS;
+  const int part = e0 / D, d0 = e0 % D;
+  const float n = (float)n_tok;
+  if constexpr (EPS == EPL) {
+#pragma unroll
+    for (int k = 0; k < EPS; ++k)
+      f[k] = KIND == HS_SUMMARY_MEAN ? acc0[k] / n : (part ? acc1[k] : acc0[k]);
+  } else {
+    static_assert(KIND == HS_SUMMARY_MEAN && EPS * 2 == EPL, "mean rows of a bf16 cache");
+    const int src = d0 / EPL;  // a lane of token group 0 holding dims [src EPL, src EPL + EPL)
+    const bool upper = (d0 % EPL) != 0;
+#pragma unroll
+    for (int k = 0; k < EPS; ++k) {
+      const float lo = __shfl(acc0[k], src), hi = __shfl(acc0[k + EPS], src);
+      f[k] = (upper ? hi : lo) / n;
+    }
   }
 }
 
