@@ -100,6 +100,7 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i) {
 
 struct TopkShared {
   __attribute__((aligned(16))) uint32_t hist[kBins];
+  __attribute__((aligned(16))) float xpose[kThreads * kRegKeys];  // scores, transposed
   uint32_t cand_key[kWaves][kMaxCand];   // threshold-bin keys (up to kMaxCand + 7 read)
   int32_t cand_slot[kWaves][kMaxCand];
   uint32_t tie_cnt[kRegKeys][kWaves];
@@ -304,9 +305,13 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   float v[KPT];
   uint32_t kmax = 0, kmin_inv = 0;
   if (n > 0) {
+    // coalesced loads (thread t: candidates u * 256 + t), transposed through
+    // LDS to the contiguous ownership
 #pragma unroll
     for (int u = 0; u < KPT; ++u)  // unconditional (clamped) loads that overlap
-      v[u] = published(&sc[min(c0 + u, n - 1)]);
+      v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) sh.xpose[u * kThreads + tid] = v[u];
     const int nch = (n + kRowsPerWG - 1) / kRowsPerWG;
     const int32_t* ck = reinterpret_cast<const int32_t*>(
         p.chunk_keys + (int64_t)unit * select_chunks(p.n_slots_max) * 2);
@@ -322,6 +327,17 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   if (p.window > 0) {
     const int64_t lo_tok = (int64_t)ug.T - p.window;
     w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / p.block_size);
+  }
+  __syncthreads();  // transposed scores and cleared histogram
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < KPT; u += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(&sh.xpose[c0 + u]);
+      v[u] = x.x;
+      v[u + 1] = x.y;
+      v[u + 2] = x.z;
+      v[u + 3] = x.w;
+    }
   }
   // keys; candidates past n get key 0 (below every finite score's key)
   uint32_t kr[KPT];
@@ -342,7 +358,6 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   if (k_eff == n_valid && k_eff > 0) {
     keep_all = true;
   } else if (k_eff > 0) {
-    __syncthreads();  // histogram cleared
     remaining = k_eff;
     if (kmax == kmin) {
       prefix = kmax;
