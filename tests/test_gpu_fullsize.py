@@ -1,7 +1,8 @@
 """GPU parity at the five workloads' full sizes, on sampled units.
 
-The whole problem runs on the GPU through the C ABI, in the launch
-configuration the benchmark times; the oracle recomputes a few units one by
+The whole problem runs on the GPU through the C ABI, both as separate
+stage calls and as the benchmark's single-launch step (hs_decode_step); the
+oracle recomputes a few units one by
 one from regenerated inputs (the generator is counter-based, so any unit's
 rows can be drawn alone). Ids follow the near-tie rule, outputs the per-row
 relative bound.
@@ -57,7 +58,23 @@ def test_full_size_single_layer(cfg):
     ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
     assert np.all(cnt > 0) and np.all(cnt <= w.max_selected)
     outs = [out.cpu().double().numpy()]
-    ties = check_units(w, P, q, ids, cnt, outs, sample_units(w, 4 if cfg > 1 else 4))
+    units = sample_units(w, 4)
+    ties = check_units(w, P, q, ids, cnt, outs, units)
+    # the benchmark's step: hs_decode_step (refresh of the last block + fused
+    # selection and attention) on the same inputs; its tables, ids and outputs
+    # equal the separate calls' bit for bit, and so pass the same oracle check
+    last = (w.T - 1) // w.S
+    ids2_t, cnt2_t, out2_t, _ = P.decode_step(q, summ, last)
+    torch.cuda.synchronize()
+    ids2, cnt2 = ids2_t.cpu().numpy(), cnt2_t.cpu().numpy()
+    assert np.array_equal(cnt2, cnt)
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            assert np.array_equal(ids2[b, g, :cnt[b, g]], ids[b, g, :cnt[b, g]]), (b, g)
+    out2 = out2_t.cpu().double().numpy()
+    assert np.array_equal(out2, outs[0]), float(np.abs(out2 - outs[0]).max())
+    check_units(w, P, q, ids2, cnt2, [out2], units)
+    log("config %d: hs_decode_step equals the separate calls; oracle checks pass" % cfg)
     # needle recall (reported, not asserted): needle blocks kept by the selection
     if w.needles:
         hit = tot = 0
