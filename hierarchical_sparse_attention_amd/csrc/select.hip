@@ -6,28 +6,30 @@
 namespace hs {
 namespace {
 
+// dynamic LDS: [bitmap][keys of the general path][id list, out_cap + kWave]
 template <typename TE, int D, int KIND, int G>
-__global__ __launch_bounds__(kThreads) void k_select(SelectParams p) {
+__global__ __launch_bounds__(kThreads) void k_select(SelectParams p, int list_off) {
   __shared__ TopkShared sh;
   extern __shared__ uint32_t dyn[];
-  select_task<TE, D, KIND, G>(p, blockIdx.y, blockIdx.x, gridDim.x, sh, dyn);
+  select_task<TE, D, KIND, G>(p, blockIdx.y, blockIdx.x, gridDim.x, sh, dyn,
+                              reinterpret_cast<int32_t*>(dyn + list_off));
 }
 
 template <typename TE, int D, int KIND>
-hipError_t launch_g(const SelectParams& p, dim3 grid, size_t lds, hipStream_t s) {
+hipError_t launch_g(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_select<TE, D, KIND, 1>), grid, dim3(kThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((k_select<TE, D, KIND, 2>), grid, dim3(kThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((k_select<TE, D, KIND, 4>), grid, dim3(kThreads), lds, s, p); break;
-    default: hipLaunchKernelGGL((k_select<TE, D, KIND, 8>), grid, dim3(kThreads), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((k_select<TE, D, KIND, 1>), grid, dim3(kThreads), lds, s, p, list_off); break;
+    case 2: hipLaunchKernelGGL((k_select<TE, D, KIND, 2>), grid, dim3(kThreads), lds, s, p, list_off); break;
+    case 4: hipLaunchKernelGGL((k_select<TE, D, KIND, 4>), grid, dim3(kThreads), lds, s, p, list_off); break;
+    default: hipLaunchKernelGGL((k_select<TE, D, KIND, 8>), grid, dim3(kThreads), lds, s, p, list_off); break;
   }
   return hipGetLastError();
 }
 
 template <typename TE, int D>
-hipError_t launch_k(const SelectParams& p, dim3 grid, size_t lds, hipStream_t s) {
-  return p.kind == HS_SUMMARY_MEAN ? launch_g<TE, D, HS_SUMMARY_MEAN>(p, grid, lds, s)
-                                   : launch_g<TE, D, HS_SUMMARY_MINMAX>(p, grid, lds, s);
+hipError_t launch_k(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
+  return p.kind == HS_SUMMARY_MEAN ? launch_g<TE, D, HS_SUMMARY_MEAN>(p, grid, lds, list_off, s)
+                                   : launch_g<TE, D, HS_SUMMARY_MINMAX>(p, grid, lds, list_off, s);
 }
 
 }  // namespace
@@ -42,11 +44,14 @@ size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max) {
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   const dim3 grid(select_chunks(p.n_slots_max),
                   p.kv.batch * p.kv.num_kv_heads);
-  const size_t lds = select_lds_bytes(p.out_blocks_max, p.n_slots_max);
+  const int list_off = (int)(select_lds_bytes(p.out_blocks_max, p.n_slots_max) / sizeof(uint32_t));
+  const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.out_cap + kWave);
   const bool bf = p.kv.elem_bytes == 2;
   if (p.kv.head_dim == 64)
-    return bf ? launch_k<bf16_t, 64>(p, grid, lds, s) : launch_k<float, 64>(p, grid, lds, s);
-  return bf ? launch_k<bf16_t, 128>(p, grid, lds, s) : launch_k<float, 128>(p, grid, lds, s);
+    return bf ? launch_k<bf16_t, 64>(p, grid, lds, list_off, s)
+              : launch_k<float, 64>(p, grid, lds, list_off, s);
+  return bf ? launch_k<bf16_t, 128>(p, grid, lds, list_off, s)
+            : launch_k<float, 128>(p, grid, lds, list_off, s);
 }
 
 }  // namespace hs

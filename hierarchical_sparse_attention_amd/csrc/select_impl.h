@@ -99,7 +99,8 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i) {
 }
 
 struct TopkShared {
-  __attribute__((aligned(16))) uint32_t hist[kBins];
+  // bins, then one dummy bin per lane that absorbs the counts of absent keys
+  __attribute__((aligned(16))) uint32_t hist[kBins + kWave];
   __attribute__((aligned(16))) float xpose[kThreads * kRegKeys];  // scores, transposed
   uint32_t cand_key[kWaves][kMaxCand];   // threshold-bin keys (up to kMaxCand + 7 read)
   int32_t cand_slot[kWaves][kMaxCand];
@@ -110,6 +111,8 @@ struct TopkShared {
   uint32_t red[3][kWaves];
   __attribute__((aligned(16))) uint32_t bcast[4];
   __attribute__((aligned(16))) uint32_t wcnt[kWaves];
+  uint32_t kbits[kThreads * kRegKeys / 32];  // threshold-bin candidates ranked into the top-k
+  uint32_t n_cand;                           // threshold-bin candidates gathered
   int last;
 };
 
@@ -306,30 +309,42 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   uint32_t kmax = 0, kmin_inv = 0;
   if (n > 0) {
     // coalesced loads (thread t: candidates u * 256 + t), transposed through
-    // LDS to the contiguous ownership
+    // LDS to the contiguous ownership; thread t < nch loads chunk t's key
+    // range in the same round trip
 #pragma unroll
     for (int u = 0; u < KPT; ++u)  // unconditional (clamped) loads that overlap
       v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) sh.xpose[u * kThreads + tid] = v[u];
     const int nch = (n + kRowsPerWG - 1) / kRowsPerWG;
     const int32_t* ck = reinterpret_cast<const int32_t*>(
         p.chunk_keys + (int64_t)unit * select_chunks(p.n_slots_max) * 2);
+    for (int ch = tid; ch < nch; ch += kThreads) {
+      kmax = max(kmax, (uint32_t)published_i32(&ck[2 * ch]));
+      kmin_inv = max(kmin_inv, (uint32_t)published_i32(&ck[2 * ch + 1]));
+    }
 #pragma unroll
-    for (int ch = 0; ch < KPT; ++ch) {
-      const int cc = min(ch, nch - 1);
-      kmax = max(kmax, (uint32_t)published_i32(&ck[2 * cc]));
-      kmin_inv = max(kmin_inv, (uint32_t)published_i32(&ck[2 * cc + 1]));
+    for (int u = 0; u < KPT; ++u) sh.xpose[u * kThreads + tid] = v[u];
+    kmax = wave_max_u(kmax);
+    kmin_inv = wave_max_u(kmin_inv);
+    if ((tid & (kWave - 1)) == 0) {
+      sh.red[1][tid / kWave] = kmax;
+      sh.red[2][tid / kWave] = kmin_inv;
     }
   }
   for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+  if (tid < kThreads * KPT / 32) sh.kbits[tid] = 0u;
+  if (tid == 0) sh.n_cand = 0u;
   int w0 = ug.nb;  // blocks w0 .. nb-1 hold the window's tokens
   if (p.window > 0) {
     const int64_t lo_tok = (int64_t)ug.T - p.window;
     w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / p.block_size);
   }
-  __syncthreads();  // transposed scores and cleared histogram
+  __syncthreads();  // transposed scores, key ranges, cleared histogram and bits
   if (n > 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      kmax = max(kmax, sh.red[1][w]);
+      kmin_inv = max(kmin_inv, sh.red[2][w]);
+    }
 #pragma unroll
     for (int u = 0; u < KPT; u += 4) {
       const float4 x = *reinterpret_cast<const float4*>(&sh.xpose[c0 + u]);
@@ -369,17 +384,19 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
         const int db = min(kDigitBits, 32 - resolved);
         const int shift = 32 - resolved - db;
         const uint32_t dmask = (1u << db) - 1u;
+        const uint32_t dummy = kBins + (tid & (kWave - 1));
         if (first) {
           // every present key shares the leading `resolved` bits: no test
 #pragma unroll
           for (int u = 0; u < KPT; ++u)
-            if (kr[u] != 0) atomicAdd(&sh.hist[(kr[u] >> shift) & dmask], 1u);
+            atomicAdd(&sh.hist[kr[u] != 0 ? (kr[u] >> shift) & dmask : dummy], 1u);
         } else {
           const uint32_t hi_pre = prefix >> (32 - resolved);
 #pragma unroll
-          for (int u = 0; u < KPT; ++u)
-            if (kr[u] != 0 && (kr[u] >> (32 - resolved)) == hi_pre)
-              atomicAdd(&sh.hist[(kr[u] >> shift) & dmask], 1u);
+          for (int u = 0; u < KPT; ++u) {
+            const bool in = kr[u] != 0 && (kr[u] >> (32 - resolved)) == hi_pre;
+            atomicAdd(&sh.hist[in ? (kr[u] >> shift) & dmask : dummy], 1u);
+          }
         }
         __syncthreads();
         in_bin = take_digit_flat(sh, 1 << db, shift, prefix, remaining);
@@ -404,71 +421,59 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
     keep |= (uint32_t)kept << u;
     inb |= (uint32_t)(rank_bin && in) << u;
   }
-  if (rank_bin) {  // uniform
+  if (rank_bin && resolved == 32) {  // uniform
+    // every bin key equals the threshold: the first `remaining` of them in
+    // candidate order are kept
     uint32_t m;
-    uint32_t pos = wg_excl_scan((uint32_t)__popc(inb), sh.scan_tot[1], &m);  // m == in_bin
-    if (resolved == 32) {
-      // every bin key equals the threshold: the first `remaining` of them in
-      // candidate order are kept
+    uint32_t pos = wg_excl_scan((uint32_t)__popc(inb), sh.scan_tot[1], &m);
 #pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if ((inb >> u) & 1u) keep |= (pos++ < remaining ? 1u : 0u) << u;
-    } else {
-      // a few distinct keys: gather them in candidate order, then each owner
-      // ranks its own bin keys (key desc, candidate asc) against all of them
-      uint32_t* ckey = &sh.cand_key[0][0];
-      int32_t* cslot = &sh.cand_slot[0][0];
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if ((inb >> u) & 1u) {
-          ckey[pos] = kr[u];
-          cslot[pos] = c0 + u;
-          ++pos;
-        }
-      __syncthreads();
-      if (inb) {  // this thread's bin keys, ranked against the first 16 then the rest
-        uint32_t kj[16];
-        int cj[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          kj[i] = ckey[i];
-          cj[i] = cslot[i];
-        }
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-          if (!((inb >> u) & 1u)) continue;
-          const uint32_t kt = kr[u];
-          const int ct = c0 + u;
-          uint32_t rank = 0;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            rank += ((uint32_t)i < m && (kj[i] > kt || (kj[i] == kt && cj[i] < ct))) ? 1u : 0u;
-          for (uint32_t j = 16; j < m; ++j) {  // crowded bins only
-            const uint32_t k2 = ckey[j];
-            const int c2 = cslot[j];
-            rank += (k2 > kt || (k2 == kt && c2 < ct)) ? 1u : 0u;
-          }
-          if (rank < remaining) keep |= 1u << u;
-        }
-      }
+    for (int u = 0; u < KPT; ++u)
+      if ((inb >> u) & 1u) keep |= (pos++ < remaining ? 1u : 0u) << u;
+  } else if (rank_bin) {  // uniform
+    // at most kMaxCand distinct-enough keys: gather them (any order), rank
+    // each against all of them (key desc, candidate asc) and set the bits of
+    // those ranked below `remaining`
+    uint32_t* ckey = &sh.cand_key[0][0];
+    int32_t* cslot = &sh.cand_slot[0][0];
+    for (uint32_t bits = inb; bits != 0; bits &= bits - 1) {  // usually no or one pass
+      const int u = __builtin_ctz(bits);
+      const uint32_t slot = atomicAdd(&sh.n_cand, 1u);
+      const uint32_t vb = __float_as_uint(sh.xpose[c0 + u] + 0.f);  // the key of kr[u]
+      ckey[slot] = vb ^ ((uint32_t)((int32_t)vb >> 31) | 0x80000000u);
+      cslot[slot] = c0 + u;
     }
+    __syncthreads();
+    if ((uint32_t)tid < in_bin) {
+      const uint32_t kt = ckey[tid];
+      const int ct = cslot[tid];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < in_bin; ++j) {
+        const uint32_t k2 = ckey[j];
+        const int c2 = cslot[j];
+        rank += (k2 > kt || (k2 == kt && c2 < ct)) ? 1u : 0u;
+      }
+      if (rank < remaining) atomicOr(&sh.kbits[ct >> 5], 1u << (ct & 31));
+    }
+    __syncthreads();
+    keep |= (sh.kbits[c0 >> 5] >> (c0 & 31)) & ((1u << KPT) - 1u);
   }
-  // ascending ids: a kept block's position is its rank in candidate order
+  // ascending ids: a kept block's position is its rank in candidate order;
+  // the 16 writes are unconditional, a candidate that is not kept (or does not
+  // fit) goes to the lane's trash slot list[cap + lane]
   uint32_t total;
-  uint32_t at = wg_excl_scan((uint32_t)__popc(keep), sh.scan_tot[2], &total);
+  const uint32_t at = wg_excl_scan((uint32_t)__popc(keep), sh.scan_tot[2], &total);
   const uint32_t cap = (uint32_t)p.out_cap;
+  const uint32_t trash = cap + (uint32_t)(tid & (kWave - 1));
 #pragma unroll
-  for (int u = 0; u < KPT; ++u)
-    if ((keep >> u) & 1u) {
-      if (at < cap) {
-        if (list) list[at] = c0 + u;
-        if (gids) gids[at] = c0 + u;
-      }
-      ++at;
-    }
+  for (int u = 0; u < KPT; ++u) {
+    const uint32_t pos = at + __popc(keep & ((1u << u) - 1u));
+    list[((keep >> u) & 1u) && pos < cap ? pos : trash] = c0 + u;
+  }
   const int cnt = (int)min(total, cap);
-  if (gcnt && tid == 0) *gcnt = cnt;
   __syncthreads();  // the list is complete; scan slots may be reused
+  if (gids)
+    for (int i = tid; i < cnt; i += kThreads) gids[i] = list[i];
+  if (gcnt && tid == 0) *gcnt = cnt;
   return cnt;
 }
 
@@ -982,12 +987,13 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
 // One task of the selection kernel: score a chunk, arrive on the unit's
 // counter (nchunks tasks); the last one to arrive selects and writes the
 // unit's ids and count to global memory.
+// list: LDS staging of the id list (out_cap + kWave entries).
 template <typename TE, int D, int KIND, int G>
 __device__ __forceinline__ void select_task(const SelectParams& p, int unit, int chunk, int nchunks,
-                                            TopkShared& sh, uint32_t* dyn) {
+                                            TopkShared& sh, uint32_t* dyn, int32_t* list) {
   score_chunk<TE, D, KIND, G>(p, unit, chunk, sh);
   if (!arrive_last(counter_of(p.counters, unit), nchunks, &sh.last)) return;
-  select_from_scores(p, unit, unit_geom(p, unit), sh, dyn, nullptr,
+  select_from_scores(p, unit, unit_geom(p, unit), sh, dyn, list,
                      p.out_ids + (int64_t)unit * p.out_cap, p.out_cnt + unit);
 }
 

@@ -49,7 +49,8 @@ union StepShared {
   DecodeShared<D, G> d;
 };
 
-// dynamic LDS words: [bitmap][keys of the general top-k path][id list]
+// dynamic LDS words: [bitmap][keys of the general top-k path][id list, list_cap
+// entries and kWave trash slots]
 size_t step_list_offset(int32_t out_blocks_max, int32_t n_slots_max) {
   return select_lds_bytes(out_blocks_max, n_slots_max) / sizeof(uint32_t);
 }
@@ -136,13 +137,13 @@ hipError_t launch_k(const StepParams& p, size_t lds, int list_off, hipStream_t s
 int step_chunks(int32_t n_slots_max) { return select_chunks(n_slots_max); }
 
 bool step_fits(int32_t out_blocks_max, int32_t n_slots_max, int32_t list_cap) {
-  const size_t words = step_list_offset(out_blocks_max, n_slots_max) + (size_t)list_cap;
+  const size_t words = step_list_offset(out_blocks_max, n_slots_max) + (size_t)list_cap + kWave;
   return words * sizeof(uint32_t) <= kMaxDynLds;
 }
 
 hipError_t launch_step(const StepParams& p, hipStream_t s) {
   const int list_off = (int)step_list_offset(p.sel.out_blocks_max, p.sel.n_slots_max);
-  const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.list_cap);
+  const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.list_cap + kWave);
   const bool bf = p.sel.kv.elem_bytes == 2;
   if (p.sel.kv.head_dim == 64)
     return bf ? launch_k<bf16_t, 64>(p, lds, list_off, s) : launch_k<float, 64>(p, lds, list_off, s);
