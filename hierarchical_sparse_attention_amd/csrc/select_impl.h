@@ -39,7 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;  // summary rows in flight per lane group while scoring
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kBinsPerThread = kBins / kThreads;
@@ -410,17 +410,24 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   }
   const bool take_bin = in_bin > 0 && in_bin == remaining;
   const bool rank_bin = !keep_all && !take_bin && in_bin > 0;
-  // bit u of keep / inb: candidate c0 + u is kept / in the threshold bin
-  uint32_t keep = 0, inb = 0;
+  // bit u of keep / inb: candidate c0 + u is kept / in the threshold bin.
+  // Present keys are never 0, so "present" is the candidate range alone, and
+  // prefix <= k <= pmax is one unsigned compare.
+  constexpr uint32_t kFull = (1u << KPT) - 1u;
+  const auto from = [&](int lo) {  // bits u with c0 + u >= lo
+    const int s = lo - c0;
+    return s <= 0 ? kFull : (s >= KPT ? 0u : (kFull << s) & kFull);
+  };
+  const uint32_t present = kFull & ~from(n), in_window = from(w0);
+  uint32_t above = 0, in_range = 0;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int c = c0 + u;
-    const uint32_t k = kr[u];
-    const bool in = k != 0 && k >= prefix && k <= pmax;
-    const bool kept = c < n && (keep_all || c >= w0 || k > pmax || (take_bin && in));
-    keep |= (uint32_t)kept << u;
-    inb |= (uint32_t)(rank_bin && in) << u;
+    above |= (uint32_t)(kr[u] > pmax) << u;
+    in_range |= (uint32_t)(kr[u] - prefix <= pmax - prefix) << u;
   }
+  uint32_t keep =
+      present & (keep_all ? kFull : (in_window | above | (take_bin ? in_range : 0u)));
+  const uint32_t inb = rank_bin ? in_range & present : 0u;
   if (rank_bin && resolved == 32) {  // uniform
     // every bin key equals the threshold: the first `remaining` of them in
     // candidate order are kept
