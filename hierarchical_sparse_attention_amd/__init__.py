@@ -27,7 +27,8 @@ KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 # Names declared in include/hs_attn.h; the CPU tests check that each is exported.
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
-           "hs_select_decode", "hs_decode_step", "hs_status_string", "hs_version")
+           "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_status_string",
+           "hs_version")
 
 
 class HsError(RuntimeError):
@@ -84,9 +85,11 @@ def lib() -> ctypes.CDLL:
                                        vp, vp, sz, vp]
         L.hs_decode_step.argtypes = [P(hs_select_params), P(hs_kv_cache), vp, P(hs_summaries),
                                      P(hs_summaries), i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.hs_append_kv.argtypes = [P(hs_kv_cache), vp, vp, vp, vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
-                     "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step"):
+                     "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step",
+                     "hs_append_kv"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -213,6 +216,17 @@ def hs_build_summaries(kv: KVCache, out: Summaries, block_begin: int = 0, stream
     _check("hs_build_summaries",
            lib().hs_build_summaries(ctypes.byref(ks), block_begin, ctypes.byref(os_),
                                     _stream(stream)))
+
+
+def hs_append_kv(kv: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """Write one token per sequence (k_new, v_new [B][Hkv][d] in the cache
+    dtype) at position seq_lens[b] and advance kv.seq_lens on the device."""
+    for t in (k_new, v_new):
+        if t.dtype != kv.k_pool.dtype or not t.is_contiguous():
+            raise ValueError("k_new / v_new must be contiguous and in the cache dtype")
+    ks = kv.struct()
+    _check("hs_append_kv", lib().hs_append_kv(ctypes.byref(ks), _ptr(k_new), _ptr(v_new),
+                                              _ptr(kv.seq_lens), _stream(stream)))
 
 
 def hs_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,

@@ -323,6 +323,22 @@ hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin, const h
   return from_hip(hs::launch_build_summaries(p, static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_new,
+                       int32_t* seq_lens, void* stream) {
+  const hs_status st = check_kv(kv, true, true);
+  if (st != HS_OK) return st;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return HS_ERR_INVALID_ARG;
+  if (!seq_lens || seq_lens != kv->seq_lens) return HS_ERR_INVALID_ARG;
+  hs::AppendParams p;
+  p.kv = view_of(kv);
+  p.k_pool = static_cast<uint8_t*>(const_cast<void*>(kv->k_pool));
+  p.v_pool = static_cast<uint8_t*>(const_cast<void*>(kv->v_pool));
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.seq_lens = seq_lens;
+  return from_hip(hs::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
 hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
                            const hs_summaries* fine, const hs_summaries* coarse,
                            int32_t* block_ids, int32_t* num_selected, void* workspace,

@@ -178,6 +178,17 @@ struct SummParams {
 };
 hipError_t launch_build_summaries(const SummParams& p, hipStream_t s);
 
+// Decode-time append of one token per sequence.
+struct AppendParams {
+  KvView kv;                 // shapes, page table (its pools are the ones written)
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const void* k_new;         // [B][Hkv][d] in the cache dtype
+  const void* v_new;
+  int32_t* seq_lens;         // [B] read, advanced by one where the token was written
+};
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
 // One selection level (fused scoring + top-k + window).
 struct SelectParams {
   KvView kv;                 // shapes + seq_lens

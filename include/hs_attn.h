@@ -176,6 +176,24 @@ hs_status hs_decode_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
 hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin,
                              const hs_summaries* out, void* stream);
 
+/* Decode-time append ([SGL 2.2] each decode step writes the new token's K/V
+ * into the paged cache through the page table; [HiSp 3.1] the per-block
+ * table is then updated: refresh the growing block with hs_build_summaries
+ * or hs_decode_step, block_begin = ceil(T_b / S) - 1 with the new T_b).
+ * For every sequence b, t = seq_lens[b] is read on the device; if
+ * 0 <= t < kv->max_seq_len and page_table[b][t / P] is a valid page id, the
+ * rows k_new[b][g][:] and v_new[b][g][:] of every KV head g are written to
+ * slot t % P of that page of k_pool and v_pool, and seq_lens[b] becomes
+ * t + 1. A sequence at capacity (or with an invalid page id) is left
+ * unchanged: nothing is written and its length is not advanced, which the
+ * caller can see by reading seq_lens.
+ *   k_new, v_new : dtype[batch][Hkv][head_dim], 16-byte aligned.
+ *   seq_lens     : must be kv->seq_lens (the one array that is advanced).
+ * Requires both pools. Later calls on the same stream see the new rows and
+ * lengths. */
+hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_new,
+                       int32_t* seq_lens, void* stream);
+
 /* Stage 2 - query-guided block selection ([SGL 2.2] decode phase step a;
  * [QSA 2.2] three-level scheme; [QSA 3.2] selection on the GPU; [QSA 5.1]
  * fp32 scores).

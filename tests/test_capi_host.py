@@ -152,3 +152,19 @@ def test_entry_points_fail_before_launch():
     assert L.hs_build_summaries(None, 0, ctypes.byref(fine), None) == hs.HS_ERR_INVALID_ARG
     assert L.hs_select_workspace_size(None, ctypes.byref(kv), ctypes.byref(fine), None,
                                       ctypes.byref(n)) == hs.HS_ERR_INVALID_ARG
+
+
+def test_append_rejects_bad_arguments_before_launch():
+    L = hs.lib()
+    kv = kv_struct()
+    sl = kv.seq_lens
+    # missing or misaligned rows, a length array other than the cache's, no V pool
+    assert L.hs_append_kv(ctypes.byref(kv), None, FAKE, sl, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_append_kv(ctypes.byref(kv), FAKE, FAKE + 4, sl, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_append_kv(ctypes.byref(kv), FAKE, FAKE, sl + 64, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_append_kv(ctypes.byref(kv), FAKE, FAKE, None, None) == hs.HS_ERR_INVALID_ARG
+    kv_nov = kv_struct(v_pool=0)
+    assert L.hs_append_kv(ctypes.byref(kv_nov), FAKE, FAKE, sl, None) == hs.HS_ERR_INVALID_ARG
+    kv_bad = kv_struct(head_dim=96)
+    assert L.hs_append_kv(ctypes.byref(kv_bad), FAKE, FAKE, sl, None) == hs.HS_ERR_UNSUPPORTED
+    assert L.hs_append_kv(None, FAKE, FAKE, sl, None) == hs.HS_ERR_INVALID_ARG
