@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--path", choices=["fused", "separate"], default="fused")
+    ap.add_argument("--loop-steps", type=int, default=64,
+                    help="steps of the timed decode loop (append + step); 0 skips it")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
                     help="copy: plain device-to-device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -296,6 +298,13 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     qheads = w.batch * w.hq
 
+    # ------------------------------------------ decode loop (append + step)
+    loop = (decode_loop(w, copies[0], pt, stream, args.event_steps, min(args.loop_steps, w.T - 1))
+            if args.loop_steps > 0 else None)
+    if loop:
+        log("decode loop: %.4f ms per step (append %.4f ms)" % (loop["ms_per_step"],
+                                                                  loop["append_ms"]))
+
     # ----------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
@@ -336,9 +345,63 @@ def main():
                                  "traffic": measured_traffic("hs_sparse_decode", w.name)}},
         "summary_build": {"ms": build_avg, "GBps": build_bytes / build_avg / 1e6},
         "warm_ms_per_step_single_copy": warm_ms,
+        "decode_loop": loop,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def decode_loop(w, c, pt, stream, reps, steps=64):
+    """Decode-time cache maintenance, timed: the copy's sequences restart
+    `steps` tokens short of T; every step appends the next token's K and V
+    (hs_append_kv; the rows already cached at that position, so the pools end
+    unchanged) and runs hs_decode_step with the refresh of the growing block.
+    The whole loop is one captured graph whose first node resets seq_lens."""
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    kv0 = c["kv"]
+    t0 = w.T - steps
+    sl_init = torch.full((w.batch,), t0, dtype=torch.int32, device="cuda")
+    sl = sl_init.clone()
+    kv = hs.KVCache(kv0.k_pool, kv0.v_pool, pt, sl, w.T)
+    pos = torch.arange(t0, w.T, device="cuda")
+    k_new, v_new = [], []
+    for pool, dst in ((kv0.k_pool, k_new), (kv0.v_pool, v_new)):
+        rows = [pool[pt[b, pos // w.page_size].long(), :, pos % w.page_size] for b in range(w.batch)]
+        dst.append(torch.stack(rows, 1).contiguous())  # [steps][B][Hkv][d]
+    k_new, v_new = k_new[0], v_new[0]
+
+    def body(with_step):
+        sl.copy_(sl_init)
+        for i in range(steps):
+            hs.hs_append_kv(kv, k_new[i], v_new[i], stream=stream)
+            if with_step:
+                hs.hs_decode_step(kv, c["q"], c["fine"], w.top_k, w.window, (t0 + i) // w.S,
+                                  c["ids"], c["cnt"], c["out"], c["ws_f"], stream=stream)
+
+    out = {}
+    for name, with_step in (("loop", True), ("append", False)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            body(with_step)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            g.replay()
+            for e0, e1 in evs:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / steps
+        del g
+    assert sl.cpu().tolist() == [w.T] * w.batch
+    return {"steps_per_loop": steps, "start_len": t0, "ms_per_step": out["loop"],
+            "query_heads_per_s": w.batch * w.hq / (out["loop"] * 1e-3),
+            "append_ms": out["append"]}
 
 
 def cpu_baseline(w, seconds):
