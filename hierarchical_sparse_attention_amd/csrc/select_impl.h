@@ -454,28 +454,38 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
       const uint32_t kt = ckey[tid];
       const int ct = cslot[tid];
       uint32_t rank = 0;
-      for (uint32_t j = 0; j < in_bin; ++j) {
-        const uint32_t k2 = ckey[j];
-        const int c2 = cslot[j];
-        rank += (k2 > kt || (k2 == kt && c2 < ct)) ? 1u : 0u;
+      for (uint32_t j0 = 0; j0 < in_bin; j0 += 8) {  // 8 loads per LDS round trip
+        uint32_t k2[8];
+        int c2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          k2[i] = ckey[j0 + i];  // slots past in_bin (< kWaves * kMaxCand) are ignored
+          c2[i] = cslot[j0 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rank += (j0 + i < in_bin && (k2[i] > kt || (k2[i] == kt && c2[i] < ct))) ? 1u : 0u;
       }
       if (rank < remaining) atomicOr(&sh.kbits[ct >> 5], 1u << (ct & 31));
     }
     __syncthreads();
     keep |= (sh.kbits[c0 >> 5] >> (c0 & 31)) & ((1u << KPT) - 1u);
   }
-  // ascending ids: a kept block's position is its rank in candidate order;
-  // the 16 writes are unconditional, a candidate that is not kept (or does not
-  // fit) goes to the lane's trash slot list[cap + lane]
+  // ascending ids: a kept block's position is its rank in candidate order.
+  // The window's candidates [w0, n) are all kept and come last, so they are
+  // written cooperatively; each thread writes its other kept candidates (a
+  // few) in a loop over their bits.
   uint32_t total;
-  const uint32_t at = wg_excl_scan((uint32_t)__popc(keep), sh.scan_tot[2], &total);
+  const uint32_t rest = keep & ~in_window;
+  const uint32_t at = wg_excl_scan((uint32_t)__popc(rest), sh.scan_tot[2], &total);
+  const int n_win = max(0, n - max(w0, 0));  // window candidates present
   const uint32_t cap = (uint32_t)p.out_cap;
-  const uint32_t trash = cap + (uint32_t)(tid & (kWave - 1));
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const uint32_t pos = at + __popc(keep & ((1u << u) - 1u));
-    list[((keep >> u) & 1u) && pos < cap ? pos : trash] = c0 + u;
-  }
+  uint32_t pos = at;
+  for (uint32_t bits = rest; bits != 0; bits &= bits - 1, ++pos)
+    if (pos < cap) list[pos] = c0 + __builtin_ctz(bits);
+  for (int i = tid; i < n_win; i += kThreads)
+    if (total + (uint32_t)i < cap) list[total + i] = w0 + i;
+  total += (uint32_t)n_win;
   const int cnt = (int)min(total, cap);
   __syncthreads();  // the list is complete; scan slots may be reused
   if (gids)
