@@ -347,3 +347,71 @@ def test_shared_selection_across_layers():
         assert np.allclose(out, want, rtol=1e-12, atol=1e-13)
         own.append(oracle.select_unit(ql, Kl, w.T, "mean", w.S, w.top_k, w.window).ids.tolist())
     assert own[1] != sel.ids.tolist() or own[2] != sel.ids.tolist()
+
+
+# ------------------------------------------------ LRU cache of selected blocks
+from oracle.block_cache import cache_step  # noqa: E402
+
+
+def test_block_cache_hand_worked_example():
+    """Capacity 4, steps 0-3, worked by hand from the rule (empty slots first,
+    then least recently used; ties by slot index)."""
+    blk, st = [-1] * 4, [-1] * 4
+    # step 0: {5, 9} -> slots 0, 1 (empty, lowest index first); all new
+    blk, st, slot_of, miss, h, m, d = cache_step(blk, st, [5, 9], 0)
+    assert (blk, st, slot_of, miss, h, m, d) == ([5, 9, -1, -1], [0, 0, -1, -1], [0, 1], [5, 9],
+                                                 0, 2, 2)
+    # step 1: {2, 9, 11} -> 9 hits (stamp 0 == step - 1), 2 and 11 take the empty 2, 3
+    blk, st, slot_of, miss, h, m, d = cache_step(blk, st, [2, 9, 11], 1)
+    assert (blk, st, slot_of, miss, h, m, d) == ([5, 9, 2, 11], [0, 1, 1, 1], [2, 1, 3], [2, 11],
+                                                 1, 2, 2)
+    # step 2: {3, 11} -> 11 hits; 3 evicts block 5 (stamp 0, the oldest)
+    blk, st, slot_of, miss, h, m, d = cache_step(blk, st, [3, 11], 2)
+    assert (blk, st, slot_of, miss, h, m, d) == ([3, 9, 2, 11], [2, 1, 1, 2], [0, 3], [3],
+                                                 1, 1, 1)
+    # step 3: {1, 4, 9} -> 9 hits (stamp 1 != 2: new relative to step 2);
+    # 1 and 4 take slots 2 (stamp 1) then 0 (stamp 2, tie with 3 broken by index)
+    blk, st, slot_of, miss, h, m, d = cache_step(blk, st, [1, 4, 9], 3)
+    assert (blk, st, slot_of, miss, h, m, d) == ([4, 9, 1, 11], [3, 3, 3, 2], [2, 0, 1], [1, 4],
+                                                 1, 2, 3)
+
+
+@pytest.mark.parametrize("seed,cap,k,nb", [(1, 8, 4, 20), (2, 12, 6, 40), (3, 64, 16, 100),
+                                           (4, 5, 5, 9)])
+def test_block_cache_invariants_against_step_history(seed, cap, k, nb):
+    """Random drifting selections: after every step the cache holds the whole
+    selection once; hits + misses = |S_t|; the step difference equals the set
+    difference (when capacity >= 2k); evictions follow LRU against a last-use
+    record kept independently from the step history; empty slots go first."""
+    rng = np.random.default_rng(seed)
+    blk, st = [-1] * cap, [-1] * cap
+    last_use = {}
+    prev = set()
+    cur = set(rng.choice(nb, size=k, replace=False).tolist())
+    for t in range(40):
+        if t:  # keep most of the previous selection, swap a few blocks
+            keep = set(rng.choice(sorted(cur), size=max(0, k - int(rng.integers(0, k // 2 + 2))),
+                                  replace=False).tolist())
+            pool = [b for b in range(nb) if b not in keep]
+            cur = keep | set(rng.choice(pool, size=k - len(keep), replace=False).tolist())
+        ids = sorted(cur)
+        before = dict((b, s) for s, b in enumerate(blk) if b >= 0)
+        empties = sum(1 for b in blk if b < 0)
+        nblk, nst, slot_of, miss, h, m, d = cache_step(blk, st, ids, t)
+        # the selection is cached, each block once, at the reported slots
+        assert sorted(b for b in nblk if b >= 0) == sorted(set(b for b in nblk if b >= 0))
+        assert all(nblk[slot_of[j]] == b and nst[slot_of[j]] == t for j, b in enumerate(ids))
+        assert h + m == len(ids) and m == len(miss) and miss == sorted(set(ids) - set(before))
+        if cap >= 2 * k:
+            assert d == len(set(ids) - prev)
+        evicted = [b for b in before if b not in nblk]
+        if m <= empties:
+            assert not evicted
+        kept_unused = [b for b in nblk if b >= 0 and b in before and b not in cur]
+        for e in evicted:
+            for f in kept_unused:
+                assert last_use[e] <= last_use[f], (t, e, f)
+        for b in ids:
+            last_use[b] = t
+        prev = set(ids)
+        blk, st = nblk, nst
