@@ -27,8 +27,13 @@ KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 # Names declared in include/hs_attn.h; the CPU tests check that each is exported.
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
-           "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_status_string",
-           "hs_version")
+           "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_block_cache_update",
+           "hs_status_string", "hs_version")
+
+
+class hs_block_cache(ctypes.Structure):
+    _fields_ = [("slot_block", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("capacity", ctypes.c_int32)]
 
 
 class HsError(RuntimeError):
@@ -86,10 +91,12 @@ def lib() -> ctypes.CDLL:
         L.hs_decode_step.argtypes = [P(hs_select_params), P(hs_kv_cache), vp, P(hs_summaries),
                                      P(hs_summaries), i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.hs_append_kv.argtypes = [P(hs_kv_cache), vp, vp, vp, vp]
+        L.hs_block_cache_update.argtypes = [P(hs_block_cache), i32, i32, vp, vp, i32, vp, vp, vp,
+                                            vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
                      "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step",
-                     "hs_append_kv"):
+                     "hs_append_kv", "hs_block_cache_update"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -227,6 +234,45 @@ def hs_append_kv(kv: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=N
     ks = kv.struct()
     _check("hs_append_kv", lib().hs_append_kv(ctypes.byref(ks), _ptr(k_new), _ptr(v_new),
                                               _ptr(kv.seq_lens), _stream(stream)))
+
+
+@dataclass
+class BlockCache:
+    """LRU index of selected blocks: slot_block and slot_stamp int32
+    [units][capacity], both -1 when empty."""
+    slot_block: torch.Tensor
+    slot_stamp: torch.Tensor
+
+    @staticmethod
+    def empty(units: int, capacity: int, device="cuda") -> "BlockCache":
+        return BlockCache(torch.full((units, capacity), -1, dtype=torch.int32, device=device),
+                          torch.full((units, capacity), -1, dtype=torch.int32, device=device))
+
+    def struct(self) -> hs_block_cache:
+        return hs_block_cache(_ptr(self.slot_block), _ptr(self.slot_stamp),
+                              int(self.slot_block.shape[-1]))
+
+
+def hs_block_cache_update(cache: BlockCache, step: int, block_ids: torch.Tensor,
+                          num_selected: torch.Tensor, slot_of: torch.Tensor,
+                          miss_blocks: torch.Tensor, stats: torch.Tensor, stream=None) -> None:
+    """block_ids / slot_of / miss_blocks int32 [..][max_selected] with
+    units rows; num_selected int32 [units]; stats int32 [units][3]."""
+    for t in (cache.slot_block, cache.slot_stamp, block_ids, num_selected, slot_of, miss_blocks,
+              stats):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("block cache arrays must be contiguous int32")
+    units = num_selected.numel()
+    ms = block_ids.shape[-1]
+    if cache.slot_block.numel() != units * cache.slot_block.shape[-1] or \
+            block_ids.numel() != units * ms or slot_of.numel() != units * ms or \
+            miss_blocks.numel() != units * ms or stats.numel() != units * 3:
+        raise ValueError("block cache arrays do not match the number of units")
+    cs = cache.struct()
+    _check("hs_block_cache_update",
+           lib().hs_block_cache_update(ctypes.byref(cs), units, step, _ptr(block_ids),
+                                       _ptr(num_selected), ms, _ptr(slot_of), _ptr(miss_blocks),
+                                       _ptr(stats), _stream(stream)))
 
 
 def hs_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,

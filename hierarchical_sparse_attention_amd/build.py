@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhs_attn.so")
-SOURCES = ["capi.hip", "summaries.hip", "select.hip", "decode.hip", "step.hip", "append.hip"]
+SOURCES = ["capi.hip", "summaries.hip", "select.hip", "decode.hip", "step.hip", "append.hip",
+           "block_cache.hip"]
 ARCH = os.environ.get("HS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

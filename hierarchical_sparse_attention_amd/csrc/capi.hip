@@ -339,6 +339,31 @@ hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_n
   return from_hip(hs::launch_append(p, static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_block_cache_update(const hs_block_cache* cache, int32_t units, int32_t step,
+                                const int32_t* block_ids, const int32_t* num_selected,
+                                int32_t max_selected, int32_t* slot_of, int32_t* miss_blocks,
+                                int32_t* stats, void* stream) {
+  if (!cache || !cache->slot_block || !cache->slot_stamp) return HS_ERR_INVALID_ARG;
+  if (!block_ids || !num_selected || !slot_of || !miss_blocks || !stats) return HS_ERR_INVALID_ARG;
+  if (units < 1 || units > 65535 || step < 0 || step == 0x7FFFFFFF) return HS_ERR_INVALID_ARG;
+  if (max_selected < 1 || cache->capacity < max_selected) return HS_ERR_INVALID_ARG;
+  if (max_selected > hs::kMaxCacheSelected || cache->capacity > hs::kMaxCacheSlots)
+    return HS_ERR_UNSUPPORTED;
+  hs::CacheParams p;
+  p.slot_block = cache->slot_block;
+  p.slot_stamp = cache->slot_stamp;
+  p.capacity = cache->capacity;
+  p.units = units;
+  p.step = step;
+  p.max_selected = max_selected;
+  p.ids = block_ids;
+  p.counts = num_selected;
+  p.slot_of = slot_of;
+  p.miss_blocks = miss_blocks;
+  p.stats = stats;
+  return from_hip(hs::launch_cache_update(p, static_cast<hipStream_t>(stream)));
+}
+
 hs_status hs_select_blocks(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
                            const hs_summaries* fine, const hs_summaries* coarse,
                            int32_t* block_ids, int32_t* num_selected, void* workspace,

@@ -189,6 +189,22 @@ struct AppendParams {
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
+// LRU cache of selected blocks: one step of every unit.
+struct CacheParams {
+  int32_t* slot_block;       // [units][capacity]
+  int32_t* slot_stamp;       // [units][capacity]
+  int32_t capacity;
+  int32_t units, step, max_selected;
+  const int32_t* ids;        // [units][max_selected] ascending
+  const int32_t* counts;     // [units]
+  int32_t* slot_of;          // [units][max_selected]
+  int32_t* miss_blocks;      // [units][max_selected]
+  int32_t* stats;            // [units][3]: hits, misses, step difference
+};
+constexpr int kMaxCacheSlots = 1024;
+constexpr int kMaxCacheSelected = 2048;
+hipError_t launch_cache_update(const CacheParams& p, hipStream_t s);
+
 // One selection level (fused scoring + top-k + window).
 struct SelectParams {
   KvView kv;                 // shapes + seq_lens

@@ -194,6 +194,45 @@ hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin,
 hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_new,
                        int32_t* seq_lens, void* stream);
 
+/* LRU cache of selected blocks and the step difference ([SGL 3.2] sparse
+ * diff kernel: consecutive steps select largely the same blocks; a cache pool
+ * a few times the top-k is kept least-recently-used; each step takes the
+ * difference from the previous selection, finds the cached blocks, loads the
+ * misses and updates the cache index). With the whole cache in HBM this is
+ * the index alone: which block each slot holds, and which selected blocks a
+ * host tier would have to load.
+ * Per unit, `capacity` slots hold a block id (-1 = empty) and the step at
+ * which that block was last selected (-1 for empty slots); the caller starts
+ * from all -1 (e.g. a 0xFF fill) and passes increasing steps.
+ * One call = one step `step` for every unit, with this step's selection
+ * (block_ids / num_selected as written by hs_select_blocks, ids ascending):
+ *   - a selected block found in a slot is a hit; its stamp becomes `step`;
+ *   - the misses, in ascending block order, take the slots not hit at this
+ *     step in order of (stamp ascending, slot index ascending): empty slots
+ *     first, then the least recently used; they get stamp `step`;
+ *   slot_of     : int32[units][max_selected], the slot of each selected block;
+ *   miss_blocks : int32[units][max_selected], the missed blocks, ascending
+ *                 (the loads of a host tier); entries past the misses are
+ *                 left untouched;
+ *   stats       : int32[units][3] = hits, misses, |S_t minus S_(t-1)| (the
+ *                 selected blocks whose slot did not carry stamp step - 1;
+ *                 the set difference from the previous call's selection when
+ *                 capacity >= 2 * max_selected, as with the pages' 2-4 x
+ *                 top-k pool).
+ * Requires max_selected <= capacity <= 1024, max_selected <= 2048, units in
+ * [1, 65535], 0 <= step < INT32_MAX. Calls that share a cache must not
+ * overlap. */
+typedef struct {
+  int32_t* slot_block;  /* [units][capacity] */
+  int32_t* slot_stamp;  /* [units][capacity] */
+  int32_t capacity;
+} hs_block_cache;
+
+hs_status hs_block_cache_update(const hs_block_cache* cache, int32_t units, int32_t step,
+                                const int32_t* block_ids, const int32_t* num_selected,
+                                int32_t max_selected, int32_t* slot_of, int32_t* miss_blocks,
+                                int32_t* stats, void* stream);
+
 /* Stage 2 - query-guided block selection ([SGL 2.2] decode phase step a;
  * [QSA 2.2] three-level scheme; [QSA 3.2] selection on the GPU; [QSA 5.1]
  * fp32 scores).

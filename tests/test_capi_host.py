@@ -168,3 +168,22 @@ def test_append_rejects_bad_arguments_before_launch():
     kv_bad = kv_struct(head_dim=96)
     assert L.hs_append_kv(ctypes.byref(kv_bad), FAKE, FAKE, sl, None) == hs.HS_ERR_UNSUPPORTED
     assert L.hs_append_kv(None, FAKE, FAKE, sl, None) == hs.HS_ERR_INVALID_ARG
+
+
+def test_block_cache_rejects_bad_arguments_before_launch():
+    L = hs.lib()
+    c = hs.hs_block_cache(FAKE, FAKE + 4096, 580)
+    args = lambda **o: [o.get(k, v) for k, v in (  # noqa: E731
+        ("cache", ctypes.byref(c)), ("units", 32), ("step", 0), ("ids", FAKE), ("cnt", FAKE),
+        ("ms", 145), ("slot_of", FAKE), ("miss", FAKE), ("stats", FAKE), ("stream", None))]
+    assert L.hs_block_cache_update(*args(cache=None)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(units=0)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(step=-1)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(step=2 ** 31 - 1)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(ids=None)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(stats=None)) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_block_cache_update(*args(ms=581)) == hs.HS_ERR_INVALID_ARG  # capacity < max_selected
+    big = hs.hs_block_cache(FAKE, FAKE + 4096, 1025)
+    assert L.hs_block_cache_update(*args(cache=ctypes.byref(big))) == hs.HS_ERR_UNSUPPORTED
+    empty = hs.hs_block_cache(None, FAKE, 580)
+    assert L.hs_block_cache_update(*args(cache=ctypes.byref(empty))) == hs.HS_ERR_INVALID_ARG
