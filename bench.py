@@ -305,6 +305,10 @@ def main():
         log("decode loop: %.4f ms per step (append %.4f ms)" % (loop["ms_per_step"],
                                                                   loop["append_ms"]))
 
+    cache = block_cache_timing(w, stream, args.event_steps)
+    log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
+                                                             cache["capacity"]))
+
     # ----------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
@@ -346,6 +350,7 @@ def main():
         "summary_build": {"ms": build_avg, "GBps": build_bytes / build_avg / 1e6},
         "warm_ms_per_step_single_copy": warm_ms,
         "decode_loop": loop,
+        "block_cache": cache,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -402,6 +407,60 @@ def decode_loop(w, c, pt, stream, reps, steps=64):
     return {"steps_per_loop": steps, "start_len": t0, "ms_per_step": out["loop"],
             "query_heads_per_s": w.batch * w.hq / (out["loop"] * 1e-3),
             "append_ms": out["append"]}
+
+
+def block_cache_timing(w, stream, reps, steps=16, keep=0.85):
+    """hs_block_cache_update at the workload's shape (B * Hkv units, max_selected
+    ids, 4 x max_selected slots) over `steps` seeded drifting selections: each
+    step keeps about `keep` of a unit's previous blocks (the pages report 80-90 %
+    overlap between consecutive steps) and draws the rest anew. One captured
+    graph: the cache is refilled with -1, then the steps run in order."""
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    ms, units = w.max_selected, w.units
+    rng = np.random.default_rng(w.seed + 99)
+    ids = np.full((steps, units, ms), -1, np.int32)
+    cnt = np.zeros((steps, units), np.int32)
+    for u in range(units):
+        cur = np.sort(rng.choice(w.nb, size=ms - 1, replace=False))
+        for t in range(steps):
+            if t:
+                kept = cur[rng.random(len(cur)) < keep]
+                pool = np.setdiff1d(np.arange(w.nb), kept)
+                cur = np.sort(np.concatenate([kept, rng.choice(pool, size=ms - 1 - len(kept),
+                                                               replace=False)]))
+            ids[t, u, :len(cur)] = cur
+            cnt[t, u] = len(cur)
+    d_ids = torch.from_numpy(ids).cuda()
+    d_cnt = torch.from_numpy(cnt).cuda()
+    cache = hs.BlockCache.empty(units, 4 * ms)
+    slot_of = torch.empty((units, ms), dtype=torch.int32, device="cuda")
+    miss = torch.empty_like(slot_of)
+    stats = torch.empty((steps, units, 3), dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        cache.slot_block.fill_(-1)
+        cache.slot_stamp.fill_(-1)
+        for t in range(steps):
+            hs.hs_block_cache_update(cache, t, d_ids[t], d_cnt[t], slot_of, miss, stats[t],
+                                     stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        g.replay()
+        for e0, e1 in evs:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    ms_call = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / steps
+    st = stats.cpu().numpy()[1:]  # steps after the first (cold) one
+    return {"capacity": 4 * ms, "units": units, "steps": steps, "ms_per_call": ms_call,
+            "mean_overlap": float(1.0 - st[:, :, 2].sum() / st[:, :, :2].sum()),
+            "miss_rate": float(st[:, :, 1].sum() / st[:, :, :2].sum())}
 
 
 def cpu_baseline(w, seconds):

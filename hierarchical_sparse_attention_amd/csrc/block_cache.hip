@@ -18,8 +18,7 @@
 namespace hs {
 namespace {
 
-constexpr int kCacheThreads = 256;
-constexpr int32_t kHitKey = 0x7FFFFFFF;  // eviction key of a slot hit at this step
+constexpr int kCacheThreads = 1024;  // one slot (capacity <= 1024) and one sort pair per thread
 
 __device__ __forceinline__ uint32_t wg_excl_sum(uint32_t x, uint32_t* tot, uint32_t* total) {
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
@@ -40,19 +39,28 @@ __device__ __forceinline__ uint32_t wg_excl_sum(uint32_t x, uint32_t* tot, uint3
   return off + inc - x;
 }
 
+// Slots are ordered for eviction by the 64-bit key (stamp + 1, slot index):
+// empty slots (stamp -1) first, then least recently used, ties by index.
+// Slots hit at this step, and the padding up to a power of two, sort last.
+__host__ __device__ inline int sort_size(int c) {
+  int n = 1;
+  while (n < c) n <<= 1;
+  return n;
+}
+
 // One workgroup per unit. Dynamic LDS: ids, slot of each id, "stamp was t-1"
-// flags and the miss order (max_selected each), then the slots' eviction keys
-// (capacity).
+// flags and the miss order (max_selected each), then the eviction keys
+// (sort_size(capacity) 64-bit words, 8-byte aligned).
 __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
   extern __shared__ int32_t lds[];
   __shared__ uint32_t tot[kCacheThreads / kWave];
-  __shared__ uint32_t misses_total, prev_total;
   const int M = p.max_selected, C = p.capacity, t = p.step;
+  const int N = sort_size(C);
   int32_t* ids = lds;
   int32_t* sof = ids + M;
   int32_t* prevf = sof + M;
   int32_t* mj = prevf + M;
-  int32_t* ekey = mj + M;
+  uint64_t* key = reinterpret_cast<uint64_t*>(mj + M);  // 16 * M bytes in: 8-byte aligned
   const int u = blockIdx.x, tid = thread_id();
   int cnt = p.counts[u];
   cnt = cnt < 0 ? 0 : (cnt > M ? M : cnt);
@@ -65,23 +73,29 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
   }
   __syncthreads();
   // hits: each slot's block is looked up in the ascending ids (binary search)
-  for (int s = tid; s < C; s += kCacheThreads) {
-    const int32_t b = sblk[s], st = sst[s];
-    int lo = 0, hi = cnt;  // first index with ids[idx] >= b
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ids[mid] < b) lo = mid + 1;
-      else hi = mid;
+  for (int s = tid; s < N; s += kCacheThreads) {
+    uint64_t k = ~0ull;
+    if (s < C) {
+      const int32_t b = sblk[s], st = sst[s];
+      int lo = 0, hi = cnt;  // first index with ids[idx] >= b
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ids[mid] < b) lo = mid + 1;
+        else hi = mid;
+      }
+      if (b >= 0 && lo < cnt && ids[lo] == b) {
+        sof[lo] = s;
+        prevf[lo] = st == t - 1 ? 1 : 0;
+        sst[s] = t;
+      } else {
+        k = ((uint64_t)(uint32_t)(st + 1) << 32) | (uint32_t)s;
+      }
     }
-    const bool hit = b >= 0 && lo < cnt && ids[lo] == b;
-    if (hit) {
-      sof[lo] = s;
-      prevf[lo] = st == t - 1 ? 1 : 0;
-    }
-    ekey[s] = hit ? kHitKey : st;
+    key[s] = k;
   }
   __syncthreads();
-  // misses numbered in ascending id order (each thread a contiguous range)
+  // misses numbered in ascending id order (each thread a contiguous range),
+  // and the count of selected blocks that carried stamp t - 1
   const int per = (cnt + kCacheThreads - 1) / kCacheThreads;
   const int j0 = min(cnt, tid * per), j1 = min(cnt, j0 + per);
   uint32_t mine = 0, prev = 0;
@@ -89,54 +103,53 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
     mine += sof[j] < 0 ? 1u : 0u;
     prev += (uint32_t)prevf[j];
   }
-  uint32_t n_miss;
+  uint32_t n_miss, n_prev;
   uint32_t r = wg_excl_sum(mine, tot, &n_miss);
   for (int j = j0; j < j1; ++j)
     if (sof[j] < 0) mj[r++] = j;
-  __syncthreads();  // tot is reused below
-  uint32_t n_prev;
+  __syncthreads();  // tot is reused
   wg_excl_sum(prev, tot, &n_prev);
-  if (tid == 0) {
-    misses_total = n_miss;
-    prev_total = n_prev;
-  }
-  __syncthreads();  // mj complete
-  // victims: slot s not hit at this step takes miss number rank(s), its place
-  // in (stamp, slot) order among those slots
-  for (int s = tid; s < C; s += kCacheThreads) {
-    const int32_t k = ekey[s];
-    if (k == kHitKey) {
-      sst[s] = t;
-      continue;
-    }
-    uint32_t rank = 0;
-    if (n_miss > 0)
-      for (int s2 = 0; s2 < C; ++s2) {
-        const int32_t k2 = ekey[s2];
-        rank += (k2 < k || (k2 == k && s2 < s)) ? 1u : 0u;
+  // eviction order: bitonic sort of the keys, ascending (only if a miss needs it)
+  if (n_miss > 0) {
+    for (int k = 2; k <= N; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < N; i += kCacheThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint64_t a = key[i], b = key[ixj];
+            const bool up = (i & k) == 0;
+            if ((a > b) == up) {
+              key[i] = b;
+              key[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
       }
-    if (rank < n_miss) {
-      const int j = mj[rank];
-      sof[j] = s;
-      sblk[s] = ids[j];
-      sst[s] = t;
-    }
+  }
+  // miss number q takes the q-th slot of the order
+  for (int q = tid; q < (int)n_miss; q += kCacheThreads) {
+    const int s = (int)(uint32_t)key[q];
+    const int j = mj[q];
+    sof[j] = s;
+    sblk[s] = ids[j];
+    sst[s] = t;
   }
   __syncthreads();  // sof complete
   for (int j = tid; j < cnt; j += kCacheThreads) p.slot_of[(int64_t)u * M + j] = sof[j];
   for (int q = tid; q < (int)n_miss; q += kCacheThreads)
     p.miss_blocks[(int64_t)u * M + q] = ids[mj[q]];
   if (tid == 0) {
-    p.stats[3 * u + 0] = cnt - (int)misses_total;
-    p.stats[3 * u + 1] = (int)misses_total;
-    p.stats[3 * u + 2] = cnt - (int)prev_total;
+    p.stats[3 * u + 0] = cnt - (int)n_miss;
+    p.stats[3 * u + 1] = (int)n_miss;
+    p.stats[3 * u + 2] = cnt - (int)n_prev;
   }
 }
 
 }  // namespace
 
 size_t cache_lds_bytes(int32_t max_selected, int32_t capacity) {
-  return sizeof(int32_t) * (4 * (size_t)max_selected + capacity);
+  return sizeof(int32_t) * 4 * (size_t)max_selected + sizeof(uint64_t) * (size_t)sort_size(capacity);
 }
 
 hipError_t launch_cache_update(const CacheParams& p, hipStream_t s) {

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import hierarchical_sparse_attention_amd as hs
 import oracle
 from gpu_helpers import (Problem, check_ids, check_rows, log, magnitudes, oracle_select,
                          unit_inputs)
@@ -93,7 +94,9 @@ def test_full_size_shared_selection_drift():
     """Config 5: 8 layers share the layer-0 selection; 16 drift steps. Every
     step's selection is computed on the GPU; the first and the last step are
     checked against the oracle on sampled units (ids, and all 8 layers'
-    outputs); the per-step set difference is reported."""
+    outputs); the per-step set difference is reported, and the device-side
+    LRU index of selected blocks (hs_block_cache_update) must report the same
+    difference for every unit at every step."""
     w = CONFIGS[5]
     log("config 5: generating and uploading %d layers" % w.layers)
     P = Problem.make(w, layers=w.layers)
@@ -101,13 +104,25 @@ def test_full_size_shared_selection_drift():
     prev = None
     diffs = []
     units = sample_units(w, 3)
+    # the device-side LRU index of selected blocks (4 x max_selected slots):
+    # its step difference must equal the host's set difference exactly
+    ms = w.max_selected
+    cache = hs.BlockCache.empty(w.units, 4 * ms)
+    slot_of = torch.empty((w.units, ms), dtype=torch.int32, device="cuda")
+    miss = torch.empty_like(slot_of)
+    stats = torch.empty((w.units, 3), dtype=torch.int32, device="cuda")
     for step in range(w.steps):
         q0 = P.q(0, step)
         ids_t, cnt_t = P.select(q0, summ)
+        hs.hs_block_cache_update(cache, step, ids_t.view(w.units, -1), cnt_t.view(-1), slot_of,
+                                 miss, stats)
         ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+        st = stats.cpu().numpy()
+        assert np.array_equal(st[:, 0] + st[:, 1], cnt.reshape(-1))
         if prev is not None:
             d = [len(set(ids[b, g, :cnt[b, g]]) - set(prev[0][b, g, :prev[1][b, g]]))
                  for b in range(w.batch) for g in range(w.hkv)]
+            assert st[:, 2].tolist() == d, step
             diffs.append((min(d), float(np.mean(d)), max(d)))
         prev = (ids, cnt)
         if step in (0, w.steps - 1):
