@@ -174,10 +174,39 @@ def summarize(rows: np.ndarray, S: int, kind: str):
     return summary_minmax(rows, S)
 
 
+def ratio_k(nb: int, ratio: float) -> int:
+    """k of a fixed-ratio selection over nb blocks: max(1, int(nb * ratio))
+    ("SparDA", section 3.2 and its inference listing in section 3.4). The
+    ratio is the float32 value a caller passes; nb * ratio is exact in float64."""
+    return max(1, int(nb * float(np.float32(ratio))))
+
+
+def length_ratio(T: int) -> float:
+    """The length schedule of "SparDA" section 3.2: no compression up to 8K
+    tokens, 15 % up to 16K, 10 % up to 32K, 5 % beyond (the page's example
+    points 16K, 32K and 128K; each length takes the ratio of the first point
+    at or above it)."""
+    if T <= 8192:
+        return 1.0
+    if T <= 16384:
+        return 0.15
+    if T <= 32768:
+        return 0.10
+    return 0.05
+
+
 def select_unit(q: np.ndarray, rows_k: np.ndarray, T: int, kind: str, S: int, top_k: int,
                 window: int, coarse_S: int = 0, top_k_coarse: int = 0,
-                coarse_kind: str = "mean", summaries=None) -> UnitSelection:
-    """Full selection of one unit from its key rows [>=T][d] (only t < T used)."""
+                coarse_kind: str = "mean", summaries=None, top_k_ratio: float = 0.0,
+                forced=None) -> UnitSelection:
+    """Full selection of one unit from its key rows [>=T][d] (only t < T used).
+
+    top_k_ratio > 0 replaces top_k by ratio_k(ceil(T / S), top_k_ratio).
+    forced: caller-supplied block ids ("SparDA" section 3.4: a small random
+    reserve set kept besides the scored top-k) unioned into the selection;
+    ids outside [0, ceil(T / S)) are ignored."""
+    if top_k_ratio > 0:
+        top_k = ratio_k(-(-T // S), top_k_ratio)
     q = _f64(q)
     G, d = q.shape
     rows = _f64(rows_k[:T])
@@ -200,7 +229,12 @@ def select_unit(q: np.ndarray, rows_k: np.ndarray, T: int, kind: str, S: int, to
     cand = np.nonzero(~np.isnan(fs))[0].astype(np.int32)
     ftop = topk(fs[cand], top_k, cand) if len(cand) else np.zeros(0, np.int32)
     kth = float(np.float32(fs[ftop[-1]])) if len(ftop) else float("nan")
-    return UnitSelection(ids=ids[:cnt].copy(), fine_scores=fs.copy(),
+    sel_ids = ids[:cnt].copy()
+    if forced is not None and len(forced):
+        f = np.asarray(forced, np.int64)
+        f = f[(f >= 0) & (f < nb)].astype(np.int32)
+        sel_ids = np.union1d(sel_ids, f).astype(np.int32)
+    return UnitSelection(ids=sel_ids, fine_scores=fs.copy(),
                          coarse_ids=cids[:ncs.value].copy(), kth_score=kth, fine_top=ftop)
 
 

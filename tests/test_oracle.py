@@ -415,3 +415,51 @@ def test_block_cache_invariants_against_step_history(seed, cap, k, nb):
             last_use[b] = t
         prev = set(ids)
         blk, st = nblk, nst
+
+
+# ------------------------------------ ratio-based k, length schedule, forced set
+def test_ratio_k_and_length_schedule_match_the_pages():
+    g = json.load(open(os.path.join(GOLD, "pages_structural.json")))
+    r = g["ratio_topk"]
+    assert oracle.ratio_k(r["n_blocks"], r["ratio"]) == r["value"]
+    for T, ratio in g["length_schedule"]["points"]:
+        assert oracle.length_ratio(T) == pytest.approx(ratio)
+    # below one block's worth the floor of 1 applies; a ratio of 1 keeps every block
+    assert oracle.ratio_k(5, 0.1) == 1 and oracle.ratio_k(37, 1.0) == 37
+    # the float32 value of the ratio is the one used (0.15 is not exact in binary)
+    assert oracle.ratio_k(1000, 0.15) == int(1000 * float(np.float32(0.15)))
+
+
+def _unit(seed, T=3000, d=64, G=2):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((G, d)), rng.standard_normal((T, d)), T
+
+
+@pytest.mark.parametrize("kind,two", [("mean", False), ("minmax", False), ("mean", True)])
+def test_forced_blocks_are_a_union(kind, two):
+    q, K, T = _unit(11)
+    S, nb = 32, -(-3000 // 32)
+    kw = dict(coarse_S=256, top_k_coarse=3) if two else {}
+    plain = oracle.select_unit(q, K, T, kind, S, 7, 100, **kw)
+    forced = np.array([-1, 0, 5, 5, nb - 1, nb, 10 ** 6, 40], np.int32)
+    got = oracle.select_unit(q, K, T, kind, S, 7, 100, forced=forced, **kw)
+    valid = {0, 5, nb - 1, 40}
+    assert set(got.ids.tolist()) == set(plain.ids.tolist()) | valid
+    assert got.ids.tolist() == sorted(set(got.ids.tolist()))
+    # nothing selected but the forced set: exactly its valid distinct ids
+    only = oracle.select_unit(q, K, T, kind, S, 0, 0, forced=forced, **kw)
+    assert only.ids.tolist() == sorted(valid)
+    # forcing every block selects every block
+    allb = oracle.select_unit(q, K, T, kind, S, 3, 0, forced=np.arange(nb), **kw)
+    assert allb.ids.tolist() == list(range(nb))
+
+
+def test_ratio_selection_keeps_ratio_k_blocks():
+    q, K, T = _unit(12)
+    S, nb = 32, -(-3000 // 32)
+    for ratio in (0.05, 0.1, 0.3):
+        k = oracle.ratio_k(nb, ratio)
+        got = oracle.select_unit(q, K, T, "minmax", S, 999, 0, top_k_ratio=ratio)
+        assert len(got.ids) == k
+        ref = oracle.select_unit(q, K, T, "minmax", S, k, 0)
+        assert got.ids.tolist() == ref.ids.tolist()
