@@ -59,7 +59,21 @@ class hs_summaries(ctypes.Structure):
 class hs_select_params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("window_tokens", ctypes.c_int32), ("top_k_coarse", ctypes.c_int32),
-                ("max_selected", ctypes.c_int32)]
+                ("max_selected", ctypes.c_int32), ("top_k_ratio", ctypes.c_float),
+                ("forced_ids", ctypes.c_void_p), ("forced_cap", ctypes.c_int32)]
+
+
+def _sel_params(num_q_heads, top_k, window, top_k_coarse, max_selected, top_k_ratio=0.0,
+                forced=None) -> hs_select_params:
+    """Selection parameters; forced: None or a contiguous int32 device tensor
+    [B][Hkv][forced_cap] of block ids (-1 = none)."""
+    if forced is not None:
+        if forced.dtype != torch.int32 or not forced.is_contiguous():
+            raise ValueError("forced ids must be a contiguous int32 tensor")
+        return hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected,
+                                float(top_k_ratio), _ptr(forced), int(forced.shape[-1]))
+    return hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected,
+                            float(top_k_ratio), None, 0)
 
 
 _lib = None
@@ -196,8 +210,9 @@ class Summaries:
 # ------------------------------------------------------------ entry points
 def hs_select_workspace_size(kv: KVCache, fine: Summaries, num_q_heads: int, top_k: int,
                              window: int, max_selected: int, coarse: Optional[Summaries] = None,
-                             top_k_coarse: int = 0) -> int:
-    p = hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected)
+                             top_k_coarse: int = 0, top_k_ratio: float = 0.0,
+                             forced: Optional[torch.Tensor] = None) -> int:
+    p = _sel_params(num_q_heads, top_k, window, top_k_coarse, max_selected, top_k_ratio, forced)
     n = ctypes.c_size_t(0)
     ks, fs = kv.struct(), fine.struct()
     cs = coarse.struct() if coarse is not None else None
@@ -278,12 +293,16 @@ def hs_block_cache_update(cache: BlockCache, step: int, block_ids: torch.Tensor,
 def hs_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
                      block_ids: torch.Tensor, num_selected: torch.Tensor,
                      workspace: torch.Tensor, coarse: Optional[Summaries] = None,
-                     top_k_coarse: int = 0, stream=None) -> None:
+                     top_k_coarse: int = 0, stream=None, top_k_ratio: float = 0.0,
+                     forced: Optional[torch.Tensor] = None) -> None:
     """q [B][Hq][d] in the cache dtype; block_ids int32 [B][Hkv][max_selected];
-    num_selected int32 [B][Hkv]; workspace a uint8 device tensor."""
+    num_selected int32 [B][Hkv]; workspace a uint8 device tensor;
+    top_k_ratio > 0 replaces top_k by max(1, int(nb_b * ratio)) per unit;
+    forced: int32 [B][Hkv][cap] block ids unioned into the selection."""
     if block_ids.dtype != torch.int32 or num_selected.dtype != torch.int32:
         raise ValueError("block_ids and num_selected must be int32")
-    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    p = _sel_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1], top_k_ratio,
+                    forced)
     ks, fs = kv.struct(), fine.struct()
     cs = coarse.struct() if coarse is not None else None
     _check("hs_select_blocks",
@@ -310,8 +329,9 @@ def hs_sparse_decode(kv: KVCache, q: torch.Tensor, block_size: int, block_ids: t
 def hs_select_decode_workspace_size(kv: KVCache, fine: Summaries, num_q_heads: int, top_k: int,
                                     window: int, max_selected: int,
                                     coarse: Optional[Summaries] = None,
-                                    top_k_coarse: int = 0) -> int:
-    p = hs_select_params(num_q_heads, top_k, window, top_k_coarse, max_selected)
+                                    top_k_coarse: int = 0, top_k_ratio: float = 0.0,
+                                    forced: Optional[torch.Tensor] = None) -> int:
+    p = _sel_params(num_q_heads, top_k, window, top_k_coarse, max_selected, top_k_ratio, forced)
     n = ctypes.c_size_t(0)
     ks, fs = kv.struct(), fine.struct()
     cs = coarse.struct() if coarse is not None else None
@@ -324,49 +344,56 @@ def hs_select_decode_workspace_size(kv: KVCache, fine: Summaries, num_q_heads: i
 
 
 def _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out, workspace,
-                        coarse, top_k_coarse, scale, stream):
+                        coarse, top_k_coarse, scale, stream, top_k_ratio=0.0, forced=None):
     if block_ids.dtype != torch.int32 or num_selected.dtype != torch.int32:
         raise ValueError("block_ids and num_selected must be int32")
     if out.dtype != torch.float32:
         raise ValueError("out must be float32")
-    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    p = _sel_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1], top_k_ratio,
+                    forced)
     ks, fs = kv.struct(), fine.struct()
     cs = coarse.struct() if coarse is not None else None
     args = (ctypes.byref(p), ctypes.byref(ks), _ptr(q), ctypes.byref(fs),
             ctypes.byref(cs) if cs is not None else None, ctypes.c_float(scale),
             _ptr(block_ids), _ptr(num_selected), _ptr(out), _ptr(workspace), workspace.numel(),
             _stream(stream))
-    keep = (p, ks, fs, cs, kv, q, fine, coarse, block_ids, num_selected, out, workspace)
+    keep = (p, ks, fs, cs, kv, q, fine, coarse, block_ids, num_selected, out, workspace, forced)
     return args, keep
 
 
 def hs_select_decode(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
                      block_ids: torch.Tensor, num_selected: torch.Tensor, out: torch.Tensor,
                      workspace: torch.Tensor, coarse: Optional[Summaries] = None,
-                     top_k_coarse: int = 0, scale: float = 0.0, stream=None) -> None:
+                     top_k_coarse: int = 0, scale: float = 0.0, stream=None,
+                     top_k_ratio: float = 0.0, forced: Optional[torch.Tensor] = None) -> None:
     """hs_select_blocks then hs_sparse_decode (block size fine.block_size) in
     one launch; same arguments and outputs as those two calls."""
     args, _ = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
-                                  workspace, coarse, top_k_coarse, scale, stream)
+                                  workspace, coarse, top_k_coarse, scale, stream, top_k_ratio,
+                                  forced)
     _check("hs_select_decode", lib().hs_select_decode(*args))
 
 
 def _decode_step_args(kv, q, fine, top_k, window, refresh_begin, block_ids, num_selected, out,
-                      workspace, coarse, top_k_coarse, scale, stream):
+                      workspace, coarse, top_k_coarse, scale, stream, top_k_ratio=0.0,
+                      forced=None):
     args, keep = _select_decode_args(kv, q, fine, top_k, window, block_ids, num_selected, out,
-                                     workspace, coarse, top_k_coarse, scale, stream)
+                                     workspace, coarse, top_k_coarse, scale, stream, top_k_ratio,
+                                     forced)
     return args[:5] + (int(refresh_begin),) + args[5:], keep
 
 
 def hs_decode_step(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, window: int,
                    refresh_begin: int, block_ids: torch.Tensor, num_selected: torch.Tensor,
                    out: torch.Tensor, workspace: torch.Tensor, coarse: Optional[Summaries] = None,
-                   top_k_coarse: int = 0, scale: float = 0.0, stream=None) -> None:
+                   top_k_coarse: int = 0, scale: float = 0.0, stream=None,
+                   top_k_ratio: float = 0.0, forced: Optional[torch.Tensor] = None) -> None:
     """hs_build_summaries from refresh_begin on (each level), then
     hs_select_decode, in one launch for a single level; the workspace is
     that of hs_select_decode."""
     args, _ = _decode_step_args(kv, q, fine, top_k, window, refresh_begin, block_ids,
-                                num_selected, out, workspace, coarse, top_k_coarse, scale, stream)
+                                num_selected, out, workspace, coarse, top_k_coarse, scale, stream,
+                                top_k_ratio, forced)
     _check("hs_decode_step", lib().hs_decode_step(*args))
 
 
@@ -406,7 +433,7 @@ def prepare_select_blocks(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: 
                           block_ids: torch.Tensor, num_selected: torch.Tensor,
                           workspace: torch.Tensor, stream, coarse: Optional[Summaries] = None,
                           top_k_coarse: int = 0) -> Prepared:
-    p = hs_select_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
+    p = _sel_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1])
     ks, fs = kv.struct(), fine.struct()
     cs = coarse.struct() if coarse is not None else None
     args = (ctypes.byref(p), ctypes.byref(ks), _ptr(q), ctypes.byref(fs),

@@ -95,6 +95,9 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
   st = check_summ(fine, kv);
   if (st != HS_OK) return st;
   if (p->top_k < 0 || p->window_tokens < 0 || p->top_k_coarse < 0) return HS_ERR_INVALID_ARG;
+  if (!(p->top_k_ratio >= 0.f && p->top_k_ratio <= 1.f)) return HS_ERR_INVALID_ARG;  // NaN too
+  if (p->forced_cap < 0 || (p->forced_cap > 0) != (p->forced_ids != nullptr))
+    return HS_ERR_INVALID_ARG;
   const bool two = p->top_k_coarse > 0;
   if (two) {
     st = check_summ(coarse, kv);
@@ -103,9 +106,12 @@ hs_status check_select(const hs_select_params* p, const hs_kv_cache* kv,
   }
   const int64_t S = fine->block_size;
   const int64_t nb = blocks_needed(kv, fine->block_size);
+  const int64_t k = p->top_k_ratio > 0.f
+                        ? std::max<int64_t>(1, (int64_t)((double)fine->max_blocks * (double)p->top_k_ratio))
+                        : p->top_k;
   const int64_t need = std::min<int64_t>(
       fine->max_blocks,
-      std::min<int64_t>(p->top_k, fine->max_blocks) + ceil_div(p->window_tokens, S) + 1);
+      std::min<int64_t>(k, fine->max_blocks) + ceil_div(p->window_tokens, S) + 1 + p->forced_cap);
   if (p->max_selected < need || p->max_selected < 1) return HS_ERR_INVALID_ARG;
 
   L->two_level = two;
@@ -214,6 +220,9 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
     sp.scores = reinterpret_cast<float*>(ws + L.off_coarse_scores);
     sp.chunk_keys = reinterpret_cast<uint32_t*>(ws + L.off_coarse_keys);
     sp.top_k = prm->top_k_coarse;
+    sp.top_k_ratio = 0.f;
+    sp.forced = nullptr;
+    sp.forced_cap = 0;
     sp.window = 0;
     sp.out_ids = gamma;
     sp.out_cnt = gamma_cnt;
@@ -236,6 +245,9 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
   sp.scores = reinterpret_cast<float*>(ws + L.off_fine_scores);
   sp.chunk_keys = reinterpret_cast<uint32_t*>(ws + L.off_fine_keys);
   sp.top_k = prm->top_k;
+  sp.top_k_ratio = prm->top_k_ratio;
+  sp.forced = prm->forced_ids;
+  sp.forced_cap = prm->forced_cap;
   sp.window = prm->window_tokens;
   sp.out_ids = block_ids;
   sp.out_cnt = num_selected;

@@ -221,6 +221,9 @@ struct SelectParams {
   float* scores;             // [units][n_slots_max]
   uint32_t* chunk_keys;      // [units][chunks][2]: largest order key, largest ~key of a chunk
   int32_t top_k;
+  float top_k_ratio;         // > 0: k = max(1, int(nb * ratio)) per unit instead of top_k
+  const int32_t* forced;     // [units][forced_cap] block ids unioned in, or null
+  int32_t forced_cap;
   int32_t window;            // tokens (0 = none)
   int32_t* out_ids;          // [units][out_cap]
   int32_t* out_cnt;          // [units]

@@ -72,6 +72,16 @@ struct UnitGeom {
   SlotMap slots;
 };
 
+// k of a unit: top_k, or max(1, int(nb * ratio)) with a ratio (nb * ratio is
+// exact in double for a float ratio and nb < 2^24, so the floor is exact).
+__device__ __forceinline__ int unit_top_k(const SelectParams& p, int nb) {
+  if (p.top_k_ratio > 0.f) {
+    const int k = (int)((double)nb * (double)p.top_k_ratio);
+    return k > 1 ? k : 1;
+  }
+  return p.top_k;
+}
+
 __device__ __forceinline__ UnitGeom unit_geom(const SelectParams& p, int unit) {
   UnitGeom u;
   u.T = clamp_len(p.kv, unit / p.kv.num_kv_heads);
@@ -339,6 +349,12 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
     w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / p.block_size);
   }
   __syncthreads();  // transposed scores, key ranges, cleared histogram and bits
+  // caller-forced blocks: bits of the candidate bitmap, read back below
+  const int32_t* forced = p.forced ? p.forced + (int64_t)unit * p.forced_cap : nullptr;
+  for (int i = tid; i < p.forced_cap; i += kThreads) {
+    const int f = forced[i];
+    if (f >= 0 && f < n) atomicOr(&sh.kbits[f >> 5], 1u << (f & 31));
+  }
   if (n > 0) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -364,7 +380,7 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   }
   const uint32_t kmin = ~kmin_inv;
   const uint32_t n_valid = n > 0 ? (uint32_t)n : 0u;
-  const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
+  const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
   // threshold bin [prefix, pmax]: keys above it are kept, `remaining` of its
   // in_bin keys are kept (ranked by key, then candidate index)
   uint32_t prefix = 0xFFFFFFFFu, pmax = 0xFFFFFFFFu, remaining = 0, in_bin = 0;
@@ -427,6 +443,10 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   }
   uint32_t keep =
       present & (keep_all ? kFull : (in_window | above | (take_bin ? in_range : 0u)));
+  if (p.forced_cap > 0) {  // uniform
+    __syncthreads();  // every forced bit is set
+    keep |= (sh.kbits[c0 >> 5] >> (c0 & 31)) & kFull & present;
+  }
   const uint32_t inb = rank_bin ? in_range & present : 0u;
   if (rank_bin && resolved == 32) {  // uniform
     // every bin key equals the threshold: the first `remaining` of them in
@@ -550,7 +570,7 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
     kmin_inv = max(kmin_inv, sh.red[2][w]);
   }
   const uint32_t kmin = ~kmin_inv;
-  const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
+  const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
   if (k_eff == 0) return;
   if (k_eff == n_valid) {  // every candidate is kept
 #pragma unroll
@@ -722,7 +742,7 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
     if (lds_keys) return sk[c];
     return slots.block_of(c) >= 0 ? order_key(published(&sc[c])) : 0u;
   };
-  const uint32_t k_eff = min((uint32_t)max(p.top_k, 0), n_valid);
+  const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
   if (k_eff == 0) return;
   const bool keep_all = k_eff == n_valid;
 
@@ -773,12 +793,14 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
   }
 }
 
-// Window blocks into the bitmap, then the bitmap as ascending ids: to `list`
+// Window and caller-forced blocks into the bitmap, then the bitmap as
+// ascending ids: to `list`
 // (LDS) and/or to `gids` / `*gcnt` (global), either may be null. Wave w
 // emits the bits of its quarter of the bitmap words, 64 bits per round (lane
 // l tests one bit, a ballot gives every set bit its position). Returns the
 // count in every thread; the list is complete when it returns.
-__device__ __forceinline__ int emit_ids(const SelectParams& p, const UnitGeom& ug, uint32_t* bitmap,
+__device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const UnitGeom& ug,
+                                        uint32_t* bitmap,
                                         TopkShared& sh, int32_t* list, int32_t* gids,
                                         int32_t* gcnt) {
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
@@ -788,6 +810,13 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, const UnitGeom& u
     const int64_t lo_tok = (int64_t)ug.T - p.window;
     const int w0 = lo_tok <= 0 ? 0 : (int)(lo_tok / S);
     for (int beta = w0 + tid; beta < nb; beta += kThreads) mark(bitmap, beta);
+  }
+  if (p.forced) {  // caller-forced blocks
+    const int32_t* forced = p.forced + (int64_t)unit * p.forced_cap;
+    for (int i = tid; i < p.forced_cap; i += kThreads) {
+      const int f = forced[i];
+      if (f >= 0 && f < nb) mark(bitmap, f);
+    }
   }
   __syncthreads();
   const int wpw = (words + kWaves - 1) / kWaves;  // words of each wave
@@ -843,7 +872,7 @@ __device__ __forceinline__ int select_from_scores(const SelectParams& p, int uni
     uint32_t* sk = dyn + (p.out_blocks_max + 31) / 32;
     topk_general(p, unit, ug, sh, bitmap, sk, p.n_slots_max <= kLdsKeys);
   }
-  return emit_ids(p, ug, bitmap, sh, list, gids, gcnt);
+  return emit_ids(p, unit, ug, bitmap, sh, list, gids, gcnt);
 }
 
 // One scoring task: rows [chunk * kRowsPerWG, (chunk + 1) * kRowsPerWG) of

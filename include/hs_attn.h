@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HS_ATTN_VERSION 1
+#define HS_ATTN_VERSION 2
 
 typedef enum {
   HS_OK = 0,
@@ -145,14 +145,28 @@ typedef struct {
  *                   [QSA 2.2]: top_k_coarse blocks of the `coarse` table, then
  *                   top_k fine blocks among the fine blocks inside them.
  *   max_selected  : row capacity of block_ids. Must be >= the largest possible
- *                   count: min(max_blocks, min(top_k, max_blocks) +
- *                   ceil(W / S) + 1). */
+ *                   count: min(max_blocks, min(K, max_blocks) + ceil(W / S)
+ *                   + 1 + forced_cap), K = top_k, or with a ratio the k of
+ *                   max_blocks blocks.
+ *   top_k_ratio   : 0 = use top_k. In (0, 1]: the fine level keeps
+ *                   k_b = max(1, int(nb_b * top_k_ratio)) blocks of unit b,
+ *                   nb_b = ceil(T_b / S), computed on the device per unit
+ *                   ([SparDA 3.2] fixed-ratio top-k and its length-dependent
+ *                   ratio; [SparDA 3.4] k = max(1, int(n * ratio))).
+ *   forced_ids    : NULL, or int32[batch][Hkv][forced_cap] block ids unioned
+ *                   into every unit's selection ([SparDA 3.4] the reserve set
+ *                   of 1-2 % random blocks kept besides the scored top-k; the
+ *                   caller draws them). Entries outside [0, nb_b) (e.g. -1
+ *                   padding) are ignored; duplicates count once. */
 typedef struct {
   int32_t num_q_heads;
   int32_t top_k;
   int32_t window_tokens;
   int32_t top_k_coarse;
   int32_t max_selected;
+  float top_k_ratio;
+  const int32_t* forced_ids;
+  int32_t forced_cap;
 } hs_select_params;
 
 /* Workspace sizes (bytes) for hs_select_blocks / hs_sparse_decode. Pure host

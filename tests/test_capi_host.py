@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert hs.hs_version() == 1
+    assert hs.hs_version() == 2
 
 
 def test_status_strings():
@@ -187,3 +187,22 @@ def test_block_cache_rejects_bad_arguments_before_launch():
     assert L.hs_block_cache_update(*args(cache=ctypes.byref(big))) == hs.HS_ERR_UNSUPPORTED
     empty = hs.hs_block_cache(None, FAKE, 580)
     assert L.hs_block_cache_update(*args(cache=ctypes.byref(empty))) == hs.HS_ERR_INVALID_ARG
+
+
+def test_select_ratio_and_forced_validation():
+    kv, fine = kv_struct(), summ()
+    base = (32, 128, 512, 0, 145)
+    P = lambda ratio=0.0, forced=None, cap=0, ms=145: hs.hs_select_params(  # noqa: E731
+        *base[:4], ms, ratio, forced, cap)
+    assert sel_size(P(), kv, fine)[0] == hs.HS_OK
+    assert sel_size(P(ratio=float("nan")), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(P(ratio=1.5), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(P(ratio=-0.1), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(P(cap=4), kv, fine)[0] == hs.HS_ERR_INVALID_ARG        # cap without ids
+    assert sel_size(P(forced=FAKE), kv, fine)[0] == hs.HS_ERR_INVALID_ARG  # ids without cap
+    # capacity counts the forced blocks: 128 + 16 + 1 + 4 = 149 rows
+    assert sel_size(P(forced=FAKE, cap=4, ms=148), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(P(forced=FAKE, cap=4, ms=149), kv, fine)[0] == hs.HS_OK
+    # with a ratio the k of max_blocks blocks counts: int(4096 * 0.05) = 204 -> 221 rows
+    assert sel_size(P(ratio=0.05, ms=220), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
+    assert sel_size(P(ratio=0.05, ms=221), kv, fine)[0] == hs.HS_OK
