@@ -305,6 +305,9 @@ def main():
         log("decode loop: %.4f ms per step (append %.4f ms)" % (loop["ms_per_step"],
                                                                   loop["append_ms"]))
 
+    sched = schedule_timing(w, copies, stream, args.event_steps)
+    log("ratio %.2f + reserve set: %.4f ms per call, %.0f GB/s" % (
+        sched["top_k_ratio"], sched["ms_per_call"], sched["GBps"]))
     cache = block_cache_timing(w, stream, args.event_steps)
     log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
                                                              cache["capacity"]))
@@ -351,6 +354,7 @@ def main():
         "warm_ms_per_step_single_copy": warm_ms,
         "decode_loop": loop,
         "block_cache": cache,
+        "ratio_and_reserve": sched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -407,6 +411,68 @@ def decode_loop(w, c, pt, stream, reps, steps=64):
     return {"steps_per_loop": steps, "start_len": t0, "ms_per_step": out["loop"],
             "query_heads_per_s": w.batch * w.hq / (out["loop"] * 1e-3),
             "append_ms": out["append"]}
+
+
+def schedule_timing(w, copies, stream, reps, reserve=0.01):
+    """hs_decode_step with the pages' length-scheduled ratio instead of a fixed
+    k (SparDA section 3.2: 5 % at 128K, so k = max(1, int(nb * 0.05))) and a
+    seeded random reserve set of `reserve` of each unit's blocks (section 3.4),
+    over the rotating input copies; time per call from events around a graph
+    of one call per copy, and algorithmic GB/s from the blocks it selected."""
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    ratio = 0.05 if w.T > 32768 else (0.10 if w.T > 16384 else 0.15)
+    nb = w.nb
+    k = max(1, int(nb * float(np.float32(ratio))))
+    r = max(1, int(nb * reserve))
+    rng = np.random.default_rng(w.seed + 7)
+    forced = np.stack([rng.choice(nb, size=r, replace=False) for _ in range(w.units)])
+    forced_t = torch.from_numpy(forced.astype(np.int32).reshape(w.batch, w.hkv, r)).cuda()
+    cap = min(nb, k + -(-w.window // w.S) + 1 + r)
+    calls, bufs = [], []
+    for c in copies:
+        ids = torch.zeros((w.batch, w.hkv, cap), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((w.batch, w.hkv), dtype=torch.int32, device="cuda")
+        out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+        n = hs.hs_select_decode_workspace_size(c["kv"], c["fine"], w.hq, w.top_k, w.window, cap,
+                                               top_k_ratio=ratio, forced=forced_t)
+        ws = hs.workspace(n, "cuda")
+        bufs.append((ids, cnt, out, ws))
+        calls.append(lambda c=c, ids=ids, cnt=cnt, out=out, ws=ws: hs.hs_decode_step(
+            c["kv"], c["q"], c["fine"], w.top_k, w.window, (w.T - 1) // w.S, ids, cnt, out, ws,
+            stream=stream, top_k_ratio=ratio, forced=forced_t))
+    with torch.cuda.stream(stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        g.replay()
+        for e0, e1 in evs:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(calls)
+    ids, cnt = bufs[0][0].cpu().numpy(), bufs[0][1].cpu().numpy()
+    lens = w.seq_lens_array()
+    esize = 2 if w.dtype == "bf16" else 4
+    tokens = sum(int(np.minimum(w.S, lens[b] - ids[b, g, :cnt[b, g]].astype(np.int64) * w.S).sum())
+                 for b in range(w.batch) for g in range(w.hkv))
+    row = w.d * 4 if w.kind == "mean" else 2 * w.d * esize
+    nbytes = (tokens * w.d * esize * 2 + w.units * w.nb * row + w.units * (w.S * w.d * esize + row)
+              + w.batch * w.hq * w.d * (esize + 4) + int(cnt.sum()) * 4)
+    return {"top_k_ratio": ratio, "k": k, "reserve_blocks": r, "max_selected": cap,
+            "mean_selected": float(cnt.mean()), "ms_per_call": ms,
+            "bytes_per_call": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def block_cache_timing(w, stream, reps, steps=16, keep=0.85):
