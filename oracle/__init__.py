@@ -238,6 +238,32 @@ def select_unit(q: np.ndarray, rows_k: np.ndarray, T: int, kind: str, S: int, to
                          coarse_ids=cids[:ncs.value].copy(), kth_score=kth, fine_top=ftop)
 
 
+def select_tokens_unit(q: np.ndarray, rows_k: np.ndarray, T: int, block_ids, S: int,
+                       top_k_tokens: int, window_tokens: int):
+    """Token-level second stage inside the selected blocks ("SparDA", section
+    2.3: after the block selection, a finer pass keeps single tokens inside the
+    chosen blocks). Candidates: the tokens t < T of blocks `block_ids`. Score
+    of token t: the sum over the G query heads of q_j . k_t (the block score
+    with the block reduced to one token), computed in float64 and rounded to
+    float32 for ranking. Kept: the first min(k, #candidates) candidates by
+    (score desc, token asc), plus the candidates among the window's tokens
+    [T - W, T). Returns (ascending token ids, scores of all T tokens with NaN
+    for non-candidates, the k-th kept score)."""
+    q = _f64(q)
+    K = _f64(rows_k[:T])
+    cand = sorted({t for b in np.asarray(block_ids, np.int64).tolist() if 0 <= b
+                   for t in range(b * S, min(b * S + S, T))})
+    scores = np.full(T, np.nan)
+    qs = q.sum(axis=0)
+    for t in cand:
+        scores[t] = float(np.float32(np.dot(K[t], qs)))
+    order = sorted(cand, key=lambda t: (-scores[t], t))
+    top = order[:max(0, min(top_k_tokens, len(order)))]
+    win = [t for t in cand if t >= T - window_tokens] if window_tokens > 0 else []
+    kth = scores[top[-1]] if top else float("nan")
+    return np.array(sorted(set(top) | set(win)), np.int32), scores, kth
+
+
 def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, T: int, ids: np.ndarray, S: int,
                 scale: Optional[float] = None) -> np.ndarray:
     """Exact softmax attention of q [G][d] over the tokens t < T of blocks `ids`."""

@@ -117,3 +117,41 @@ def test_forced_and_ratio_match_oracle(name, mode):
             check_rows(w, o1[b, g * w.G:(g + 1) * w.G], ref, what)
     log("%s/%s: %d tolerated near-tie differences, counts %s" % (name, mode, ties,
                                                                  g_cnt.reshape(-1).tolist()))
+
+
+def test_whole_coarse_block_loading():
+    """Two levels whose fine top-k covers every candidate slice: the GPU keeps
+    every fine block of its kept coarse blocks (and the window), as the oracle
+    does, through the separate calls and the fused step."""
+    w = WORK["two-level"]
+    P = problem("two-level")
+    kv = P.kvs[0]
+    q = P.q()
+    summ = P.summaries()
+    R = w.coarse_S // w.S
+    k = w.top_k_coarse * R
+    cap = min(w.nb, k + -(-w.window // w.S) + 1)
+    ids = torch.full((w.batch, w.hkv, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+    n = hs.hs_select_workspace_size(kv, summ["fine"], w.hq, k, w.window, cap, summ["coarse"],
+                                    w.top_k_coarse)
+    hs.hs_select_blocks(kv, q, summ["fine"], k, w.window, ids, cnt, hs.workspace(n, "cuda"),
+                        summ["coarse"], w.top_k_coarse)
+    out = P.decode(q, ids, cnt)
+    torch.cuda.synchronize()
+    g_ids, g_cnt = ids.cpu().numpy(), cnt.cpu().numpy()
+    o = out.cpu().double().numpy()
+    lens = w.seq_lens_array()
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            T = int(lens[b])
+            qo, K, V = unit_inputs(w, 0, b, g)
+            sel = oracle.select_unit(qo, K, T, w.kind, w.S, k, w.window, coarse_S=w.coarse_S,
+                                     top_k_coarse=w.top_k_coarse)
+            gi = g_ids[b, g, :g_cnt[b, g]]
+            nb = -(-T // w.S)
+            full = {c * R + r for c in sel.coarse_ids.tolist() for r in range(R) if c * R + r < nb}
+            assert full <= set(gi.tolist()), (b, g)
+            check_ids(w, gi, sel, magnitudes(w, qo, K, T), T, what="whole coarse (%d,%d)" % (b, g))
+            check_rows(w, o[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, w.S),
+                       "whole coarse (%d,%d)" % (b, g))

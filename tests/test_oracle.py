@@ -463,3 +463,59 @@ def test_ratio_selection_keeps_ratio_k_blocks():
         assert len(got.ids) == k
         ref = oracle.select_unit(q, K, T, "minmax", S, k, 0)
         assert got.ids.tolist() == ref.ids.tolist()
+
+
+def test_whole_coarse_block_loading_closed_form():
+    """Two levels with top_k at least the number of fine candidates ("8x256K
+    ... porting HiSparse to QSA", section 2.2, when the fine level keeps every
+    slice): the selection is every fine block inside the kept coarse blocks,
+    plus the window."""
+    q, K, T = _unit(13, T=5000)
+    S, C, kc, W = 64, 512, 3, 200
+    R = C // S
+    nb = -(-T // S)
+    sel = oracle.select_unit(q, K, T, "mean", S, kc * R, W, coarse_S=C, top_k_coarse=kc)
+    expect = {g * R + r for g in sel.coarse_ids.tolist() for r in range(R) if g * R + r < nb}
+    expect |= set(oracle.window_blocks(T, S, W).tolist())
+    assert sel.ids.tolist() == sorted(expect)
+
+
+# ------------------------------------------- token-level second stage (SparDA 2.3)
+def test_token_stage_against_dense_brute_force():
+    """Scores from one dense product over every token (a different route than
+    the per-candidate dot products), candidates masked, ranked by lexsort."""
+    q, K, T = _unit(21, T=700, d=32, G=4)
+    S = 16
+    blocks = [0, 3, 7, 20, 43]  # 43 holds the partial last block (688..699)
+    dense = (K[:T] @ q.T).sum(axis=1)  # [T]: sum over heads
+    cand = np.array([t for b in blocks for t in range(b * S, min(b * S + S, T))])
+    s32 = dense[cand].astype(np.float32)
+    for k in (1, 10, 50, len(cand), len(cand) + 5):
+        order = cand[np.lexsort((cand, -s32.astype(np.float64)))][:k]
+        ids, sc, kth = oracle.select_tokens_unit(q, K, T, blocks, S, k, 0)
+        assert ids.tolist() == sorted(order.tolist()), k
+        assert np.allclose(sc[cand], s32, rtol=1e-6)
+        assert np.all(np.isnan(np.delete(sc, cand)))
+
+
+def test_token_stage_window_ties_and_full_set():
+    q, K, T = _unit(22, T=500, d=32, G=2)
+    S = 32
+    K = K.copy()
+    qs = q.sum(axis=0)
+    K[45] = K[41] = K[40] = 10.0 * qs / np.linalg.norm(qs)  # planted exact ties, the best
+    blocks = [1, 5, 15]  # 15 holds tokens 480..499 (the window's)
+    for k, expect in ((1, [40]), (2, [40, 41]), (3, [40, 41, 45])):
+        ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, k, 0)
+        assert ids.tolist() == expect
+    # the window's candidate tokens are always kept, on top of the top-k
+    ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, 3, 30)
+    assert ids.tolist() == [40, 41, 45] + list(range(480, 500))
+    # k >= candidates: every candidate token, and attention over them equals the
+    # block-level attention over the same blocks
+    ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, 10 ** 6, 0)
+    assert ids.tolist() == [t for b in blocks for t in range(b * S, min(b * S + S, T))]
+    V = np.random.default_rng(5).standard_normal(K.shape)
+    a = oracle.attend_unit(q, K, V, T, ids, 1)
+    b = oracle.attend_unit(q, K, V, T, np.array(blocks, np.int32), S)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
