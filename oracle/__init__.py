@@ -246,9 +246,10 @@ def select_tokens_unit(q: np.ndarray, rows_k: np.ndarray, T: int, block_ids, S: 
     of token t: the sum over the G query heads of q_j . k_t (the block score
     with the block reduced to one token), computed in float64 and rounded to
     float32 for ranking. Kept: the first min(k, #candidates) candidates by
-    (score desc, token asc), plus the candidates among the window's tokens
-    [T - W, T). Returns (ascending token ids, scores of all T tokens with NaN
-    for non-candidates, the k-th kept score)."""
+    (score desc, token asc), plus every token of the window [T - W, T) (as at
+    the block level, the local window is always attended). Returns (ascending
+    token ids, scores of all T tokens with NaN for non-candidates, the k-th
+    kept score)."""
     q = _f64(q)
     K = _f64(rows_k[:T])
     cand = sorted({t for b in np.asarray(block_ids, np.int64).tolist() if 0 <= b
@@ -259,7 +260,7 @@ def select_tokens_unit(q: np.ndarray, rows_k: np.ndarray, T: int, block_ids, S: 
         scores[t] = float(np.float32(np.dot(K[t], qs)))
     order = sorted(cand, key=lambda t: (-scores[t], t))
     top = order[:max(0, min(top_k_tokens, len(order)))]
-    win = [t for t in cand if t >= T - window_tokens] if window_tokens > 0 else []
+    win = list(range(max(0, T - window_tokens), T)) if window_tokens > 0 else []
     kth = scores[top[-1]] if top else float("nan")
     return np.array(sorted(set(top) | set(win)), np.int32), scores, kth
 

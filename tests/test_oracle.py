@@ -508,9 +508,9 @@ def test_token_stage_window_ties_and_full_set():
     for k, expect in ((1, [40]), (2, [40, 41]), (3, [40, 41, 45])):
         ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, k, 0)
         assert ids.tolist() == expect
-    # the window's candidate tokens are always kept, on top of the top-k
+    # every token of the window is kept, on top of the top-k, candidate or not
     ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, 3, 30)
-    assert ids.tolist() == [40, 41, 45] + list(range(480, 500))
+    assert ids.tolist() == [40, 41, 45] + list(range(470, 500))
     # k >= candidates: every candidate token, and attention over them equals the
     # block-level attention over the same blocks
     ids, _, _ = oracle.select_tokens_unit(q, K, T, blocks, S, 10 ** 6, 0)
