@@ -28,7 +28,8 @@ KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
            "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_block_cache_update",
-           "hs_status_string", "hs_version")
+           "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_status_string",
+           "hs_version")
 
 
 class hs_block_cache(ctypes.Structure):
@@ -105,12 +106,17 @@ def lib() -> ctypes.CDLL:
         L.hs_decode_step.argtypes = [P(hs_select_params), P(hs_kv_cache), vp, P(hs_summaries),
                                      P(hs_summaries), i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.hs_append_kv.argtypes = [P(hs_kv_cache), vp, vp, vp, vp]
+        L.hs_select_tokens_workspace_size.argtypes = [P(hs_kv_cache), i32, i32, i32, i32, i32,
+                                                      i32, P(sz)]
+        L.hs_select_tokens.argtypes = [P(hs_kv_cache), vp, i32, i32, vp, vp, i32, i32, i32, vp,
+                                       vp, i32, vp, sz, vp]
         L.hs_block_cache_update.argtypes = [P(hs_block_cache), i32, i32, vp, vp, i32, vp, vp, vp,
                                             vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
                      "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step",
-                     "hs_append_kv", "hs_block_cache_update"):
+                     "hs_append_kv", "hs_block_cache_update",
+                     "hs_select_tokens_workspace_size", "hs_select_tokens"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -249,6 +255,37 @@ def hs_append_kv(kv: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=N
     ks = kv.struct()
     _check("hs_append_kv", lib().hs_append_kv(ctypes.byref(ks), _ptr(k_new), _ptr(v_new),
                                               _ptr(kv.seq_lens), _stream(stream)))
+
+
+def hs_select_tokens_workspace_size(kv: KVCache, num_q_heads: int, block_size: int,
+                                    max_selected: int, top_k_tokens: int, window: int,
+                                    max_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    ks = kv.struct()
+    _check("hs_select_tokens_workspace_size",
+           lib().hs_select_tokens_workspace_size(ctypes.byref(ks), num_q_heads, block_size,
+                                                 max_selected, top_k_tokens, window, max_tokens,
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def hs_select_tokens(kv: KVCache, q: torch.Tensor, block_size: int, block_ids: torch.Tensor,
+                     num_selected: torch.Tensor, top_k_tokens: int, window: int,
+                     token_ids: torch.Tensor, num_tokens: torch.Tensor, workspace: torch.Tensor,
+                     stream=None) -> None:
+    """Token-level second stage: block_ids int32 [B][Hkv][max_selected] from
+    hs_select_blocks; token_ids int32 [B][Hkv][max_tokens]; num_tokens int32
+    [B][Hkv]. Attend with hs_sparse_decode(kv, q, 1, token_ids, num_tokens, ...)."""
+    for t in (block_ids, num_selected, token_ids, num_tokens):
+        if t.dtype != torch.int32:
+            raise ValueError("ids and counts must be int32")
+    ks = kv.struct()
+    _check("hs_select_tokens",
+           lib().hs_select_tokens(ctypes.byref(ks), _ptr(q), q.shape[1], block_size,
+                                  _ptr(block_ids), _ptr(num_selected), block_ids.shape[-1],
+                                  top_k_tokens, window, _ptr(token_ids), _ptr(num_tokens),
+                                  token_ids.shape[-1], _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
 
 
 @dataclass

@@ -282,9 +282,99 @@ hs::DecodeParams decode_params(const hs_kv_cache* kv, const void* q, float scale
   return p;
 }
 
+// Token-level second stage: workspace [counters][scores][chunk key ranges]
+// and the level's parameters.
+struct TokenLayout {
+  int64_t units, n_slots;
+  size_t off_cnt, off_scores, off_keys, total;
+};
+
+hs_status check_tokens(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block_size,
+                       int32_t max_selected, int32_t top_k_tokens, int32_t window_tokens,
+                       int32_t max_tokens, TokenLayout* L) {
+  hs_status st = check_kv(kv, true, false);
+  if (st != HS_OK) return st;
+  group_size(kv, num_q_heads, &st);
+  if (st != HS_OK) return st;
+  if (block_size < 1 || max_selected < 1 || top_k_tokens < 0 || window_tokens < 0 ||
+      max_tokens < 1)
+    return HS_ERR_INVALID_ARG;
+  const int64_t n_slots = (int64_t)max_selected * block_size;
+  if (n_slots > (1 << 24)) return HS_ERR_UNSUPPORTED;
+  const int64_t need = std::min<int64_t>(n_slots, top_k_tokens) +
+                       std::min<int64_t>(window_tokens, kv->max_seq_len);
+  if (max_tokens < need) return HS_ERR_INVALID_ARG;
+  if (hs::select_launch_lds_bytes(kv->max_seq_len, (int32_t)n_slots, max_tokens) > (64u << 10))
+    return HS_ERR_UNSUPPORTED;
+  L->units = (int64_t)kv->batch * kv->num_kv_heads;
+  L->n_slots = n_slots;
+  L->off_cnt = 0;
+  L->off_scores = align_up(sizeof(int32_t) * hs::kCounterStride * L->units);
+  L->off_keys = align_up(L->off_scores + sizeof(float) * L->units * n_slots);
+  L->total = align_up(L->off_keys + sizeof(uint32_t) * 2 * L->units *
+                                        hs::step_chunks((int32_t)n_slots));
+  return HS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+hs_status hs_select_tokens_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
+                                          int32_t block_size, int32_t max_selected,
+                                          int32_t top_k_tokens, int32_t window_tokens,
+                                          int32_t max_tokens, size_t* bytes) {
+  if (!bytes) return HS_ERR_INVALID_ARG;
+  TokenLayout L;
+  const hs_status st = check_tokens(kv, num_q_heads, block_size, max_selected, top_k_tokens,
+                                    window_tokens, max_tokens, &L);
+  if (st == HS_OK) *bytes = L.total;
+  return st;
+}
+
+hs_status hs_select_tokens(const hs_kv_cache* kv, const void* q, int32_t num_q_heads,
+                           int32_t block_size, const int32_t* block_ids,
+                           const int32_t* num_selected, int32_t max_selected,
+                           int32_t top_k_tokens, int32_t window_tokens, int32_t* token_ids,
+                           int32_t* num_tokens, int32_t max_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  TokenLayout L;
+  hs_status st = check_tokens(kv, num_q_heads, block_size, max_selected, top_k_tokens,
+                              window_tokens, max_tokens, &L);
+  if (st != HS_OK) return st;
+  if (!q || !aligned16(q) || !block_ids || !num_selected || !token_ids || !num_tokens)
+    return HS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hs::SelectParams sp;
+  sp.kv = view_of(kv);
+  sp.q = q;
+  sp.summ = nullptr;
+  sp.kind = hs::kKindTokens;
+  sp.block_size = 1;  // a candidate is one token
+  sp.max_blocks = kv->max_seq_len;
+  sp.G = num_q_heads / kv->num_kv_heads;
+  sp.gamma = block_ids;  // the selected blocks play the coarse level: slot c is token
+  sp.gamma_cnt = num_selected;  // block_ids[c / S] * S + c % S
+  sp.gamma_cap = max_selected;
+  sp.ratio = block_size;
+  sp.n_slots_max = (int32_t)L.n_slots;
+  sp.scores = reinterpret_cast<float*>(ws + L.off_scores);
+  sp.chunk_keys = reinterpret_cast<uint32_t*>(ws + L.off_keys);
+  sp.top_k = top_k_tokens;
+  sp.top_k_ratio = 0.f;
+  sp.forced = nullptr;
+  sp.forced_cap = 0;
+  sp.window = window_tokens;
+  sp.out_ids = token_ids;
+  sp.out_cnt = num_tokens;
+  sp.out_cap = max_tokens;
+  sp.out_blocks_max = kv->max_seq_len;
+  sp.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
+  sp.refresh_begin = -1;
+  return from_hip(hs::launch_select(sp, static_cast<hipStream_t>(stream)));
+}
+
 
 const char* hs_status_string(hs_status s) {
   switch (s) {

@@ -205,6 +205,11 @@ constexpr int kMaxCacheSlots = 1024;
 constexpr int kMaxCacheSelected = 2048;
 hipError_t launch_cache_update(const CacheParams& p, hipStream_t s);
 
+// Selection-level kind beyond the public summary kinds: the candidates are
+// single tokens (block size 1) whose "summary rows" are their K rows, read
+// through the page table (the token-level second stage).
+constexpr int32_t kKindTokens = 2;
+
 // One selection level (fused scoring + top-k + window).
 struct SelectParams {
   KvView kv;                 // shapes + seq_lens
@@ -235,6 +240,8 @@ struct SelectParams {
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 // Dynamic LDS of a selection workgroup: bitmap words, then keys (general path).
 size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max);
+// Total dynamic LDS of a k_select launch (adds the staged id list).
+size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap);
 
 struct DecodeParams {
   KvView kv;

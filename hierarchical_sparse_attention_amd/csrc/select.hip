@@ -28,6 +28,7 @@ hipError_t launch_g(const SelectParams& p, dim3 grid, size_t lds, int list_off, 
 
 template <typename TE, int D>
 hipError_t launch_k(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
+  if (p.kind == kKindTokens) return launch_g<TE, D, kKindTokens>(p, grid, lds, list_off, s);
   return p.kind == HS_SUMMARY_MEAN ? launch_g<TE, D, HS_SUMMARY_MEAN>(p, grid, lds, list_off, s)
                                    : launch_g<TE, D, HS_SUMMARY_MINMAX>(p, grid, lds, list_off, s);
 }
@@ -39,6 +40,10 @@ size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max) {
   const bool general = n_slots_max > kThreads * kRegKeys;
   const size_t keys = general && n_slots_max <= kLdsKeys ? (size_t)n_slots_max : 0;
   return sizeof(uint32_t) * (words + keys);
+}
+
+size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap) {
+  return select_lds_bytes(out_blocks_max, n_slots_max) + sizeof(uint32_t) * ((size_t)out_cap + kWave);
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {

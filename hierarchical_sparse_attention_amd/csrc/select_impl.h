@@ -886,9 +886,10 @@ __device__ __forceinline__ int select_from_scores(const SelectParams& p, int uni
 template <typename TE, int D, int KIND, int G>
 __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int chunk,
                                             TopkShared& sh) {
+  constexpr bool kTok = KIND == kKindTokens;  // rows are token K rows (page table)
   using TS = typename std::conditional<KIND == HS_SUMMARY_MEAN, float, TE>::type;
   constexpr int EPS = 16 / sizeof(TS);                        // elements per 16-byte load
-  constexpr int ROW = (KIND == HS_SUMMARY_MEAN ? 1 : 2) * D;  // elements per row
+  constexpr int ROW = (KIND == HS_SUMMARY_MINMAX ? 2 : 1) * D;  // elements per row
   constexpr int LPR = ROW / EPS;                              // lanes per row
   constexpr int RPW = kWave / LPR;                            // rows per wave instruction
   constexpr int64_t kRowBytes = ROW * sizeof(TS);
@@ -906,7 +907,7 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   float coef[EPS];
   {
     const int e0 = li * EPS;                                // first element of the lane
-    const int part = KIND == HS_SUMMARY_MEAN ? 0 : e0 / D;  // 0: min (or mean), 1: max
+    const int part = KIND == HS_SUMMARY_MINMAX ? e0 / D : 0;  // 0: min (mean, token), 1: max
     const int dim0 = e0 % D;
 #pragma unroll
     for (int k = 0; k < EPS; ++k) {
@@ -915,7 +916,7 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       for (int j = 0; j < G; ++j) {
         const float qv = load_elem<TE>(
             p.q, ((int64_t)b * kv.num_kv_heads * G + g * G + j) * D + dim0 + k);
-        if (KIND == HS_SUMMARY_MEAN) c += qv;
+        if (KIND != HS_SUMMARY_MINMAX) c += qv;
         else c += part == 0 ? fminf(qv, 0.f) : fmaxf(qv, 0.f);
       }
       coef[k] = c;
@@ -940,12 +941,13 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   constexpr int kRefreshLoads = 16;
   constexpr int kTPW = kWave / (D / Vec16<TE>::EPL);  // tokens per K load instruction
   const int r0 = max(p.refresh_begin, c_wg), r1 = min(n_slots, c_wg + kRowsPerWG);
-  const bool refresh = p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1;  // uniform
+  const bool refresh = !kTok && p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1;  // uniform
   const bool early = refresh && r1 - r0 <= kWaves && p.block_size <= kRefreshLoads * kTPW;
   const int my_row = r0 + wave;
   uint4 rk[kRefreshLoads];
   uint32_t rk_ok = 0;
-  if (early && my_row < r1) rk_ok = summ_load<TE, D, kRefreshLoads>(kv, b, g, my_row, p.block_size, ug.T, rk);
+  if constexpr (!kTok)
+    if (early && my_row < r1) rk_ok = summ_load<TE, D, kRefreshLoads>(kv, b, g, my_row, p.block_size, ug.T, rk);
   const uint8_t* summ = reinterpret_cast<const uint8_t*>(p.summ) +
                         (int64_t)unit * p.max_blocks * kRowBytes;
   if (c_begin < n_slots) {  // wave-uniform
@@ -958,8 +960,14 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
         const int c = cb + u * RPW + rg;
         const int beta = c < c_end ? ug.slots.block_of(c) : -1;
         cs[u] = beta >= 0 ? c : -1;
-        r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
-                         : make_uint4(0, 0, 0, 0);
+        if constexpr (kTok) {
+          const int64_t off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
+          r[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
+                          : make_uint4(0, 0, 0, 0);
+        } else {
+          r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
+                           : make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -968,35 +976,37 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       }
     }
   }
-  if (early) {
-    __syncthreads();  // the stale scores of the refreshed rows are staged
-    if (my_row < r1) {
-      float a0[Vec16<TE>::EPL], a1[Vec16<TE>::EPL];
-      summ_reduce<TE, D, KIND, kRefreshLoads>(rk, rk_ok, a0, a1);
-      const int n_tok = min(my_row * p.block_size + p.block_size, ug.T) - my_row * p.block_size;
-      summ_store<TE, D, KIND>(const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + my_row,
-                              a0, a1, n_tok);
-      float f[EPS];
-      summ_row_elems<TE, D, KIND, EPS>(a0, a1, n_tok, f);
-      const float acc = row_dot(f);
-      if (lane == 0) sh.stage[my_row - c_wg] = acc;
-    }
-  } else if (refresh) {
-    // more blocks than waves, or long blocks: rebuild, store, and score the
-    // stored rows (device-coherent loads)
-    for (int beta = r0 + wave; beta < r1; beta += kWaves)
-      summarize_block<TE, D, KIND>(kv, const_cast<void*>(p.summ),
-                                   (int64_t)unit * p.max_blocks + beta, b, g, beta,
-                                   p.block_size, ug.T);
-    __builtin_amdgcn_s_waitcnt(0);  // rebuilt rows are stored
-    __syncthreads();                // (and the stale scores of those rows staged)
-    for (int cb = r0 + wave * RPW; cb < r1; cb += kWaves * RPW) {  // wave-uniform
-      const int c = min(cb + rg, r1 - 1);
-      const int32_t* w = reinterpret_cast<const int32_t*>(summ + c * kRowBytes + li * 16);
-      const uint4 r = make_uint4(published_i32(w), published_i32(w + 1), published_i32(w + 2),
-                                 published_i32(w + 3));
-      const float acc = row_score(r);
-      if (li == 0 && cb + rg < r1) sh.stage[cb + rg - c_wg] = acc;
+  if constexpr (!kTok) {  // refresh (summary kinds only)
+    if (early) {
+      __syncthreads();  // the stale scores of the refreshed rows are staged
+      if (my_row < r1) {
+        float a0[Vec16<TE>::EPL], a1[Vec16<TE>::EPL];
+        summ_reduce<TE, D, KIND, kRefreshLoads>(rk, rk_ok, a0, a1);
+        const int n_tok = min(my_row * p.block_size + p.block_size, ug.T) - my_row * p.block_size;
+        summ_store<TE, D, KIND>(const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + my_row,
+                                a0, a1, n_tok);
+        float f[EPS];
+        summ_row_elems<TE, D, KIND, EPS>(a0, a1, n_tok, f);
+        const float acc = row_dot(f);
+        if (lane == 0) sh.stage[my_row - c_wg] = acc;
+      }
+    } else if (refresh) {
+      // more blocks than waves, or long blocks: rebuild, store, and score the
+      // stored rows (device-coherent loads)
+      for (int beta = r0 + wave; beta < r1; beta += kWaves)
+        summarize_block<TE, D, KIND>(kv, const_cast<void*>(p.summ),
+                                     (int64_t)unit * p.max_blocks + beta, b, g, beta,
+                                     p.block_size, ug.T);
+      __builtin_amdgcn_s_waitcnt(0);  // rebuilt rows are stored
+      __syncthreads();                // (and the stale scores of those rows staged)
+      for (int cb = r0 + wave * RPW; cb < r1; cb += kWaves * RPW) {  // wave-uniform
+        const int c = min(cb + rg, r1 - 1);
+        const int32_t* w = reinterpret_cast<const int32_t*>(summ + c * kRowBytes + li * 16);
+        const uint4 r = make_uint4(published_i32(w), published_i32(w + 1), published_i32(w + 2),
+                                   published_i32(w + 3));
+        const float acc = row_score(r);
+        if (li == 0 && cb + rg < r1) sh.stage[cb + rg - c_wg] = acc;
+      }
     }
   }
   // publish the workgroup's scores with one coalesced store per thread, and

@@ -208,6 +208,37 @@ hs_status hs_build_summaries(const hs_kv_cache* kv, int32_t block_begin,
 hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_new,
                        int32_t* seq_lens, void* stream);
 
+/* Token-level second stage inside the selected blocks ([SparDA 2.3]: after
+ * the block selection, a finer pass keeps single tokens inside the chosen
+ * blocks, for very high compression). For every unit, the candidates are the
+ * tokens t < T_b of its selected blocks (block_ids / num_selected as written
+ * by hs_select_blocks with block size `block_size`). Token score, fp32,
+ * unscaled: sum over the unit's G query heads of q_j . k_t (the block score
+ * of a one-token block). Kept, ascending, without duplicates: the first
+ * min(top_k_tokens, #candidates) candidates by (score descending, token
+ * ascending), plus every token of the window [T_b - window_tokens, T_b).
+ *   token_ids  : int32[batch][Hkv][max_tokens] (entries past the count left
+ *                untouched); num_tokens : int32[batch][Hkv].
+ *   max_tokens : >= min(max_selected * block_size, top_k_tokens) +
+ *                min(window_tokens, max_seq_len).
+ * Attention over the kept tokens is hs_sparse_decode with block_size 1 and
+ * token_ids / num_tokens / max_tokens as its ids.
+ * workspace: at least hs_select_tokens_workspace_size() bytes, 16-byte
+ *   aligned and ZERO-FILLED before its first use; every call leaves its
+ *   counters at zero. Requires k_pool. HS_ERR_UNSUPPORTED when the
+ *   workgroup's LDS (a bitmap of max_seq_len bits, the candidates' keys and
+ *   the id list) would exceed 64 KiB. */
+hs_status hs_select_tokens_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
+                                          int32_t block_size, int32_t max_selected,
+                                          int32_t top_k_tokens, int32_t window_tokens,
+                                          int32_t max_tokens, size_t* bytes);
+hs_status hs_select_tokens(const hs_kv_cache* kv, const void* q, int32_t num_q_heads,
+                           int32_t block_size, const int32_t* block_ids,
+                           const int32_t* num_selected, int32_t max_selected,
+                           int32_t top_k_tokens, int32_t window_tokens, int32_t* token_ids,
+                           int32_t* num_tokens, int32_t max_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* LRU cache of selected blocks and the step difference ([SGL 3.2] sparse
  * diff kernel: consecutive steps select largely the same blocks; a cache pool
  * a few times the top-k is kept least-recently-used; each step takes the

@@ -1,0 +1,90 @@
+"""GPU parity of the token-level second stage ("SparDA" section 2.3).
+
+The block selection is the GPU's own (hs_select_blocks, tested elsewhere);
+given those blocks, hs_select_tokens keeps the top tokens inside them plus the
+window's tokens, and hs_sparse_decode with block size 1 attends over exactly
+those tokens. The oracle recomputes both from the same blocks. Token sets are
+bit-exact except for near ties: a token may differ only if its oracle score
+lies within 1e-6 * max(|s_k|, sum_j sum_i |q_j,i k_t,i|) of the k-th kept
+score s_k, and never inside the window. Every top-k path of the token level is
+covered: the register path (up to 4096 candidates), the general path with
+keys in LDS (up to 8192) and with keys in the workspace (more).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_amd as hs
+import oracle
+from gpu_helpers import Problem, check_rows, log, unit_inputs
+from synth.workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+C = CONFIGS
+CASES = {
+    # name: (workload, block top_k, token top_k, token window)
+    "regs": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000), top_k=100),
+             100, 256, 48),
+    "general-lds": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000),
+                                top_k=200), 200, 300, 0),
+    "general-ws": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, top_k=257), 257, 128, 64),
+    "f32-box": (C[1].scaled(hq=4, hkv=2, d=128, T=2500, kind="minmax", S=32, page_size=32,
+                            top_k=7), 7, 40, 20),
+}
+_P = {}
+
+
+def check_tokens(gi, ref_ids, scores, kth, qo, K, T, W, what):
+    g = gi.tolist()
+    assert g == sorted(set(g)), what
+    diff = set(g) ^ set(ref_ids.tolist())
+    mag = np.abs(K[:T]) @ np.abs(qo).sum(axis=0)
+    for t in diff:
+        assert not (t >= T - W), "%s: window token %d differs" % (what, t)
+        s = scores[t] if 0 <= t < T else float("nan")
+        assert not np.isnan(s), "%s: token %d was not a candidate" % (what, t)
+        tol = 1e-6 * max(abs(kth), mag[t])
+        assert abs(s - kth) <= tol, "%s: token %d score %.9g vs k-th %.9g" % (what, t, s, kth)
+    return len(diff)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_token_stage_matches_oracle(name):
+    w, kb, kt, wt = CASES[name]
+    if name not in _P:
+        log("setting up %s" % name)
+        _P[name] = Problem.make(w)
+    P = _P[name]
+    kv = P.kvs[0]
+    q = P.q()
+    summ = P.summaries()
+    ids, cnt = P.select(q, summ, top_k=kb)
+    ms = ids.shape[-1]
+    max_tok = min(ms * w.S, kt) + min(wt, w.T)
+    tok = torch.full((w.batch, w.hkv, max_tok), -7, dtype=torch.int32, device="cuda")
+    tcnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+    n = hs.hs_select_tokens_workspace_size(kv, w.hq, w.S, ms, kt, wt, max_tok)
+    ws = hs.workspace(n, "cuda")
+    for rep in range(2):  # the second call reuses the workspace (counters back at zero)
+        hs.hs_select_tokens(kv, q, w.S, ids, cnt, kt, wt, tok, tcnt, ws)
+    out = P.decode(q, tok, tcnt, block_size=1)
+    torch.cuda.synchronize()
+    b_ids, b_cnt = ids.cpu().numpy(), cnt.cpu().numpy()
+    t_ids, t_cnt = tok.cpu().numpy(), tcnt.cpu().numpy()
+    o = out.cpu().double().numpy()
+    lens = w.seq_lens_array()
+    ties = 0
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            T = int(lens[b])
+            qo, K, V = unit_inputs(w, 0, b, g)
+            blocks = b_ids[b, g, :b_cnt[b, g]]
+            ref, scores, kth = oracle.select_tokens_unit(qo, K, T, blocks, w.S, kt, wt)
+            gi = t_ids[b, g, :t_cnt[b, g]]
+            what = "%s unit (%d,%d)" % (name, b, g)
+            ties += check_tokens(gi, ref, scores, kth, qo, K, T, wt, what)
+            check_rows(w, o[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, 1),
+                       what)
+    log("%s: token counts %s, %d tolerated near-tie differences" % (
+        name, t_cnt.reshape(-1).tolist(), ties))
