@@ -308,6 +308,9 @@ def main():
     sched = schedule_timing(w, copies, stream, args.event_steps)
     log("ratio %.2f + reserve set: %.4f ms per call, %.0f GB/s" % (
         sched["top_k_ratio"], sched["ms_per_call"], sched["GBps"]))
+    tokens = token_stage_timing(w, copies, stream, args.event_steps)
+    log("token stage: select %.4f ms, attention %.4f ms per call" % (tokens["select_ms"],
+                                                                     tokens["decode_ms"]))
     cache = block_cache_timing(w, stream, args.event_steps)
     log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
                                                              cache["capacity"]))
@@ -354,6 +357,7 @@ def main():
         "warm_ms_per_step_single_copy": warm_ms,
         "decode_loop": loop,
         "block_cache": cache,
+        "token_stage": tokens,
         "ratio_and_reserve": sched,
         "cpu_baseline": cpu,
     }
@@ -473,6 +477,69 @@ def schedule_timing(w, copies, stream, reps, reserve=0.01):
     return {"top_k_ratio": ratio, "k": k, "reserve_blocks": r, "max_selected": cap,
             "mean_selected": float(cnt.mean()), "ms_per_call": ms,
             "bytes_per_call": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
+def token_stage_timing(w, copies, stream, reps, k_tok=1024, window=512):
+    """The token-level second stage on top of each copy's block selection (the
+    ids the timed step wrote): hs_select_tokens keeps the top `k_tok` tokens of
+    the selected blocks plus the `window` last tokens, then hs_sparse_decode
+    with block size 1 attends over them. Each call is timed with events around
+    a graph of one call per copy."""
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    ms = w.max_selected
+    max_tok = min(ms * w.S, k_tok) + min(window, w.T)
+    sel, dec, bufs = [], [], []
+    for c in copies:
+        tok = torch.zeros((w.batch, w.hkv, max_tok), dtype=torch.int32, device="cuda")
+        tcnt = torch.zeros((w.batch, w.hkv), dtype=torch.int32, device="cuda")
+        out = torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda")
+        ws_t = hs.workspace(hs.hs_select_tokens_workspace_size(c["kv"], w.hq, w.S, ms, k_tok,
+                                                               window, max_tok), "cuda")
+        ws_d = hs.workspace(hs.hs_decode_workspace_size(c["kv"], w.hq, 1, max_tok), "cuda")
+        bufs.append((tok, tcnt, out, ws_t, ws_d))
+        sel.append(lambda c=c, tok=tok, tcnt=tcnt, ws_t=ws_t: hs.hs_select_tokens(
+            c["kv"], c["q"], w.S, c["ids"], c["cnt"], k_tok, window, tok, tcnt, ws_t,
+            stream=stream))
+        dec.append(lambda c=c, tok=tok, tcnt=tcnt, out=out, ws_d=ws_d: hs.hs_sparse_decode(
+            c["kv"], c["q"], 1, tok, tcnt, out, ws_d, stream=stream))
+    res = {}
+    for name, calls in (("select_ms", sel), ("decode_ms", dec)):
+        with torch.cuda.stream(stream):
+            for call in calls:
+                call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for call in calls:
+                call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            g.replay()
+            for e0, e1 in evs:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(calls)
+        del g
+    esize = 2 if w.dtype == "bf16" else 4
+    cnt = copies[0]["cnt"].cpu().numpy()
+    ids = copies[0]["ids"].cpu().numpy()
+    lens = w.seq_lens_array()
+    cand = sum(int(np.minimum(w.S, lens[b] - ids[b, g, :cnt[b, g]].astype(np.int64) * w.S).sum())
+               for b in range(w.batch) for g in range(w.hkv))
+    kept = int(bufs[0][1].cpu().numpy().sum())
+    sel_bytes = cand * w.d * esize + w.batch * w.hq * w.d * esize + int(cnt.sum()) * 4 + kept * 4
+    dec_bytes = kept * w.d * esize * 2 + w.batch * w.hq * w.d * (esize + 4) + kept * 4
+    res.update({"k_tokens": k_tok, "window": window, "candidate_tokens": cand,
+                "kept_tokens": kept, "select_GBps": sel_bytes / (res["select_ms"] * 1e-3) / 1e9,
+                "decode_GBps": dec_bytes / (res["decode_ms"] * 1e-3) / 1e9})
+    return res
 
 
 def block_cache_timing(w, stream, reps, steps=16, keep=0.85):

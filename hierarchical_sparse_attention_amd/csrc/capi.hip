@@ -540,9 +540,11 @@ hs_status select_decode(const hs_select_params* prm, const hs_kv_cache* kv, cons
   p.dec = decode_params(kv, q, scale, fine->block_size, block_ids, num_selected,
                         prm->max_selected, out, ws + L.off_dec, L.dec);
   p.sel.refresh_begin = refresh_begin;
-  if (!hs::step_fits(p.sel.out_blocks_max, p.sel.n_slots_max, p.sel.out_cap)) {
-    // id lists too long for the fused kernel's LDS: the stages as separate
-    // launches, with the same results
+  if (!hs::step_fits(p.sel.out_blocks_max, p.sel.n_slots_max, p.sel.out_cap) ||
+      fine->block_size == 1) {
+    // id lists too long for the fused kernel's LDS, or one-token blocks (the
+    // token-list attention is compiled into the separate decode kernel only):
+    // the stages as separate launches, with the same results
     if (refresh_begin >= 0) {
       const hs_status r = hs_build_summaries(kv, refresh_begin, fine, s);
       if (r != HS_OK) return r;

@@ -10,7 +10,9 @@ constexpr int kTargetTasks = 256;  // compute units of the GPU: about one split 
 
 // One split task: the unit's count is read, its run of ids is copied into LDS
 // (written by an earlier launch, so plain loads), then attention and merge.
-template <typename TE, int D, int G>
+// TOK: block size 1, the ids are a token list (bf16 caches; the float32 path
+// handles any block size as it is).
+template <typename TE, int D, int G, bool TOK>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
   __shared__ DecodeShared<D, G> ds;
   extern __shared__ int32_t run[];
@@ -22,18 +24,24 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
   const int32_t* ids = p.ids + (int64_t)unit * p.max_selected;
   for (int i = thread_id(); i < e1 - e0; i += kDecThreads) run[i] = ids[e0 + i];
   __syncthreads();
-  decode_split<TE, D, G>(p, unit, split, run, 0, e1 - e0, ds);
+  decode_split<TE, D, G, TOK>(p, unit, split, run, 0, e1 - e0, ds);
 }
 
-template <typename TE, int D>
+template <typename TE, int D, bool TOK>
 hipError_t launch_g(const DecodeParams& p, dim3 grid, size_t lds, hipStream_t s) {
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_decode<TE, D, 1>), grid, dim3(kDecThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((k_decode<TE, D, 2>), grid, dim3(kDecThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((k_decode<TE, D, 4>), grid, dim3(kDecThreads), lds, s, p); break;
-    default: hipLaunchKernelGGL((k_decode<TE, D, 8>), grid, dim3(kDecThreads), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((k_decode<TE, D, 1, TOK>), grid, dim3(kDecThreads), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((k_decode<TE, D, 2, TOK>), grid, dim3(kDecThreads), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((k_decode<TE, D, 4, TOK>), grid, dim3(kDecThreads), lds, s, p); break;
+    default: hipLaunchKernelGGL((k_decode<TE, D, 8, TOK>), grid, dim3(kDecThreads), lds, s, p); break;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16(const DecodeParams& p, dim3 grid, size_t lds, hipStream_t s) {
+  return p.block_size == 1 ? launch_g<bf16_t, D, true>(p, grid, lds, s)
+                           : launch_g<bf16_t, D, false>(p, grid, lds, s);
 }
 
 }  // namespace
@@ -49,10 +57,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const dim3 grid(p.n_splits, p.kv.batch * p.kv.num_kv_heads);
   const size_t lds = sizeof(int32_t) * ((p.max_selected + p.n_splits - 1) / p.n_splits);
   if (p.kv.elem_bytes == 2)
-    return p.kv.head_dim == 64 ? launch_g<bf16_t, 64>(p, grid, lds, s)
-                               : launch_g<bf16_t, 128>(p, grid, lds, s);
-  return p.kv.head_dim == 64 ? launch_g<float, 64>(p, grid, lds, s)
-                             : launch_g<float, 128>(p, grid, lds, s);
+    return p.kv.head_dim == 64 ? launch_bf16<64>(p, grid, lds, s) : launch_bf16<128>(p, grid, lds, s);
+  return p.kv.head_dim == 64 ? launch_g<float, 64, false>(p, grid, lds, s)
+                             : launch_g<float, 128, false>(p, grid, lds, s);
 }
 
 }  // namespace hs

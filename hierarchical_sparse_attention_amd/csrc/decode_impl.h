@@ -153,6 +153,7 @@ template <int D>
 struct StageRegs {
   uint4 k[2][D / 32];
   uint4 v[32 / (kWave / (D / 8))];
+  uint32_t ok;  // token list mode: bit tau set if this lane's token 16 tau + r16 is valid
 };
 
 constexpr int kStagesPerChunk = kWave;  // stage-table entries filled per pass
@@ -169,8 +170,8 @@ struct DecodeShared {
 
 // Attention of the unit's query heads over the blocks ids[e0 .. e1) (a list
 // in LDS or global memory) of a bf16 cache; leaves each wave's state in
-// ds.sh for finish_split.
-template <int D, int G>
+// ds.sh for finish_split. TOK: the ids are single tokens (block size 1).
+template <int D, int G, bool TOK>
 __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, const int32_t* ids,
                                             int e0, int e1, DecodeShared<D, G>& ds) {
   constexpr int KC = D / 32;       // MFMA k-chunks per token row
@@ -200,6 +201,11 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // a 32-token stage stays inside one page when the page and block sizes are
   // multiples of 32: then one page lookup serves the whole stage
   const bool whole_page = (kv.page_size % 32 == 0) && (S % 32 == 0);
+  // block size 1 (a token list, e.g. from the token-level second stage): a
+  // stage is up to 32 consecutive list entries, each lane looks up its own
+  // token's row; tokens outside [0, T) or on an absent page are masked (their
+  // lanes read row 0 of the sequence, whose values are finite)
+  constexpr bool tok_list = TOK;
   const int64_t row_bytes = (int64_t)D * EB;
 
   // A operands: query head j in row 4 (j % 4) + j / 4 (zero rows elsewhere)
@@ -229,17 +235,34 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // Issue the loads of stage `st` of the table. Lanes of masked tokens load a
   // valid row of the same stage instead (their logits are -inf, so their p is
   // 0 and the finite V row adds nothing); an empty stage loads nothing.
+  const int64_t row0 = T > 0 ? max(row_offset(kv, b, g, 0), (int64_t)0) : 0;
+  // byte offset of the row of list entry `e` (token list mode) and its validity
+  auto token_row = [&](int e, bool& valid) {
+    const int t = ids[e];
+    int64_t off = (unsigned)t < (unsigned)T ? row_offset(kv, b, g, t) : -1;
+    valid = off >= 0;
+    return valid ? off : row0;
+  };
   auto issue = [&](int st, StageRegs<D>& R, int& len) {
     len = st_len[wave][st];
     if (len == 0) return;
     const int64_t base = st_base[wave][st];
+    R.ok = 0u;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int ti = min(16 * tau + r16, len - 1);
       // (an absent page reads row 0 instead: results are then unspecified,
       // but every access stays inside the pool)
-      const int64_t off = whole_page ? base + ti * row_bytes
-                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+      int64_t off;
+      if (tok_list) {
+        bool valid;
+        off = token_row((int)base + ti, valid);
+        R.ok |= (valid && 16 * tau + r16 < len ? 1u : 0u) << tau;
+      } else {
+        off = whole_page ? base + ti * row_bytes
+                         : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+        R.ok |= (16 * tau + r16 < len ? 1u : 0u) << tau;
+      }
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         R.k[tau][c] = *reinterpret_cast<const uint4*>(kv.k_pool + off + (32 * c + 8 * grp) * EB);
@@ -247,8 +270,14 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int ti = min(TPV * u + vt, len - 1);
-      const int64_t off = whole_page ? base + ti * row_bytes
-                                     : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+      int64_t off;
+      if (tok_list) {
+        bool valid;
+        off = token_row((int)base + ti, valid);
+      } else {
+        off = whole_page ? base + ti * row_bytes
+                         : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
+      }
       R.v[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB);
     }
   };
@@ -267,8 +296,8 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
     // register i of lane (grp, r16) holds head 4 i + grp
 #pragma unroll
     for (int i = 0; i < GR; ++i) {
-      const float x0 = r16 < len ? acc[0][i] * scale : -INFINITY;
-      const float x1 = 16 + r16 < len ? acc[1][i] * scale : -INFINITY;
+      const float x0 = (R.ok & 1u) ? acc[0][i] * scale : -INFINITY;
+      const float x1 = (R.ok & 2u) ? acc[1][i] * scale : -INFINITY;
       const float mx = group_max<16>(fmaxf(x0, x1));
       const float mn = fmaxf(m_run[i], mx);
       const float ms = mn == -INFINITY ? 0.f : mn;
@@ -313,13 +342,20 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // the stage's first row (byte offset, or its first token when a stage may
   // straddle pages) and its number of valid tokens, so that the pipeline
   // below never waits on a lookup.
+  // Token list mode: wave w owns the groups of 32 entries w, w + 4, ...
   const int spe = (S + 31) / 32;
   const int first = e0 + wave;
   const int nent = first < e1 ? (e1 - first + kDecWaves - 1) / kDecWaves : 0;
-  const int nst = nent * spe;
+  const int ngrp = (e1 - e0 + 31) / 32;
+  const int nst = tok_list ? (ngrp > wave ? (ngrp - wave + kDecWaves - 1) / kDecWaves : 0)
+                           : nent * spe;
   for (int c0 = 0; c0 < nst; c0 += kStagesPerChunk) {
     const int cst = min(kStagesPerChunk, nst - c0);
-    if (lane < cst) {
+    if (tok_list && lane < cst) {
+      const int pos = e0 + 32 * (wave + kDecWaves * (c0 + lane));  // first list entry
+      st_base[wave][lane] = pos;
+      st_len[wave][lane] = min(32, e1 - pos);
+    } else if (lane < cst) {
       const int st = c0 + lane, i = st / spe, sub = st % spe;
       const int beta = ids[first + kDecWaves * i];
       int64_t base = 0;
@@ -519,11 +555,12 @@ constexpr int f32_unroll() { return G == 8 ? 4 : 8; }
 
 // Attention of one split task over ids[e0 .. e1), then its partial and
 // arrival (the last task of the unit merges).
-template <typename TE, int D, int G>
+// TOK: the ids are single tokens (block size 1; see attend_bf16).
+template <typename TE, int D, int G, bool TOK = false>
 __device__ __forceinline__ void decode_split(const DecodeParams& p, int unit, int split,
                                              const int32_t* ids, int e0, int e1,
                                              DecodeShared<D, G>& ds) {
-  if constexpr (sizeof(TE) == 2) attend_bf16<D, G>(p, unit, ids, e0, e1, ds);
+  if constexpr (sizeof(TE) == 2) attend_bf16<D, G, TOK>(p, unit, ids, e0, e1, ds);
   else attend_f32<D, G, f32_unroll<G>()>(p, unit, ids, e0, e1, ds);
   finish_split<D, G>(p, ds.sh, unit, split);
 }

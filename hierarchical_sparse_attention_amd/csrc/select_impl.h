@@ -60,8 +60,9 @@ struct SlotMap {
     if (gamma == nullptr) return c < nb ? c : -1;
     const int gi = c / ratio;
     if (gi >= gcnt) return -1;
-    const int beta = gamma[gi] * ratio + c % ratio;
-    return beta < nb ? beta : -1;
+    const int g = gamma[gi];
+    const int beta = g * ratio + c % ratio;
+    return g >= 0 && beta < nb ? beta : -1;
   }
 };
 
@@ -784,21 +785,38 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
     for (int c = c0; c < c1; ++c) ties += key_of(c) == thr ? 1u : 0u;
   uint32_t tot;
   uint32_t rank = block_excl_scan(ties, &tot, sh);
+  // consecutive candidates share their coarse entry (ratio slots each): its
+  // id is loaded once per entry instead of once per candidate
+  int last_gi = -1, last_base = 0;
   for (int c = c0; c < c1; ++c) {
     const uint32_t k = key_of(c);
     if (k == 0) continue;
     bool keep = keep_all || k > thr;
     if (!keep && k == thr) keep = rank++ < ties_keep;
-    if (keep) mark(bitmap, slots.block_of(c));
+    if (!keep) continue;
+    int beta;
+    if (slots.gamma == nullptr) {
+      beta = c < slots.nb ? c : -1;
+    } else {
+      const int gi = c / slots.ratio;
+      if (gi != last_gi) {
+        last_gi = gi;
+        const int gg = gi < slots.gcnt ? slots.gamma[gi] : -1;
+        last_base = gg >= 0 ? gg * slots.ratio : -1;
+      }
+      beta = last_base < 0 ? -1 : last_base + c % slots.ratio;
+      beta = beta < slots.nb ? beta : -1;
+    }
+    if (beta >= 0) mark(bitmap, beta);
   }
 }
 
 // Window and caller-forced blocks into the bitmap, then the bitmap as
-// ascending ids: to `list`
-// (LDS) and/or to `gids` / `*gcnt` (global), either may be null. Wave w
-// emits the bits of its quarter of the bitmap words, 64 bits per round (lane
-// l tests one bit, a ballot gives every set bit its position). Returns the
-// count in every thread; the list is complete when it returns.
+// ascending ids: to `list` (LDS) and/or to `gids` / `*gcnt` (global), either
+// may be null. Wave w emits its quarter of the bitmap words, 64 words per
+// round: lane l takes one word, a wave prefix sum of the words' popcounts
+// gives each its first position, and the lane writes its set bits in order.
+// Returns the count in every thread; the list is complete when it returns.
 __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const UnitGeom& ug,
                                         uint32_t* bitmap,
                                         TopkShared& sh, int32_t* list, int32_t* gids,
@@ -833,19 +851,21 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const U
     pos += w2 < wave ? t : 0u;
     total += t;
   }
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   const uint32_t cap = (uint32_t)p.out_cap;
-  for (int w = w_lo; w < w_hi; w += 2) {  // wave-uniform
-    const int wl = w + (lane >> 5);
-    const bool set = wl < w_hi && ((bitmap[min(wl, w_hi - 1)] >> (lane & 31)) & 1u);
-    const uint64_t m = __ballot(set);
-    const uint32_t at = pos + (uint32_t)__popcll(m & below);
-    if (set && at < cap) {
-      const int id = wl * 32 + (lane & 31);
-      if (list) list[at] = id;
-      if (gids) gids[at] = id;
+  for (int wb = w_lo; wb < w_hi; wb += kWave) {  // wave-uniform: 64 words per round
+    const int w = wb + lane;
+    uint32_t x = w < w_hi ? bitmap[w] : 0u;
+    const uint32_t c = (uint32_t)__popc(x);
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t at = pos + incl - c;
+    for (; x != 0u; x &= x - 1u, ++at) {  // this lane's set bits, ascending
+      if (at < cap) {
+        const int id = w * 32 + __builtin_ctz(x);
+        if (list) list[at] = id;
+        if (gids) gids[at] = id;
+      }
     }
-    pos += (uint32_t)__popcll(m);
+    pos += (uint32_t)__shfl((int)incl, kWave - 1);
   }
   const int cnt = (int)min(total, cap);
   if (gcnt && tid == 0) *gcnt = cnt;
