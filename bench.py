@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--path", choices=["fused", "separate"], default="fused")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the decode loop, ratio, token-stage and block-cache figures (profiling "
+                         "runs: their launches would mix into the kernel averages)")
     ap.add_argument("--loop-steps", type=int, default=64,
                     help="steps of the timed decode loop (append + step); 0 skips it")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
@@ -300,20 +303,22 @@ def main():
 
     # ------------------------------------------ decode loop (append + step)
     loop = (decode_loop(w, copies[0], pt, stream, args.event_steps, min(args.loop_steps, w.T - 1))
-            if args.loop_steps > 0 else None)
+            if args.loop_steps > 0 and not args.headline_only else None)
     if loop:
         log("decode loop: %.4f ms per step (append %.4f ms)" % (loop["ms_per_step"],
                                                                   loop["append_ms"]))
 
-    sched = schedule_timing(w, copies, stream, args.event_steps)
-    log("ratio %.2f + reserve set: %.4f ms per call, %.0f GB/s" % (
-        sched["top_k_ratio"], sched["ms_per_call"], sched["GBps"]))
-    tokens = token_stage_timing(w, copies, stream, args.event_steps)
-    log("token stage: select %.4f ms, attention %.4f ms per call" % (tokens["select_ms"],
-                                                                     tokens["decode_ms"]))
-    cache = block_cache_timing(w, stream, args.event_steps)
-    log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
-                                                             cache["capacity"]))
+    sched = tokens = cache = None
+    if not args.headline_only:
+        sched = schedule_timing(w, copies, stream, args.event_steps)
+        log("ratio %.2f + reserve set: %.4f ms per call, %.0f GB/s" % (
+            sched["top_k_ratio"], sched["ms_per_call"], sched["GBps"]))
+        tokens = token_stage_timing(w, copies, stream, args.event_steps)
+        log("token stage: select %.4f ms, attention %.4f ms per call" % (tokens["select_ms"],
+                                                                         tokens["decode_ms"]))
+        cache = block_cache_timing(w, stream, args.event_steps)
+        log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
+                                                                 cache["capacity"]))
 
     # ----------------------------------------------------- CPU baseline
     cpu = None
