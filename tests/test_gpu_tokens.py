@@ -88,3 +88,40 @@ def test_token_stage_matches_oracle(name):
                        what)
     log("%s: token counts %s, %d tolerated near-tie differences" % (
         name, t_cnt.reshape(-1).tolist(), ties))
+
+
+@pytest.mark.parametrize("name", ["regs", "f32-box"])
+def test_token_list_attention_skips_invalid_ids(name):
+    """hs_sparse_decode with block size 1 over caller-made token lists salted
+    with -1, ids at or past T_b and huge ids: the invalid entries are skipped,
+    so the output is the attention over the valid tokens alone."""
+    w = CASES[name][0]
+    if name not in _P:
+        _P[name] = Problem.make(w)
+    P = _P[name]
+    q = P.q()
+    lens = w.seq_lens_array()
+    rng = np.random.default_rng(31)
+    n = 300
+    lists = np.full((w.batch, w.hkv, n), -1, np.int32)
+    cnts = np.zeros((w.batch, w.hkv), np.int32)
+    valid = {}
+    for b in range(w.batch):
+        T = int(lens[b])
+        for g in range(w.hkv):
+            good = np.sort(rng.choice(T, size=min(200, T), replace=False)).astype(np.int32)
+            bad = np.array([-1, T, T + 7, 2 ** 30], np.int32)
+            lst = np.concatenate([good[:50], bad[:2], good[50:], bad[2:]])
+            lists[b, g, :len(lst)] = lst
+            cnts[b, g] = len(lst)
+            valid[(b, g)] = good
+    tok = torch.from_numpy(lists).cuda()
+    tc = torch.from_numpy(cnts).cuda()
+    out = P.decode(q, tok, tc, block_size=1)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    for (b, g), good in valid.items():
+        T = int(lens[b])
+        qo, K, V = unit_inputs(w, 0, b, g)
+        ref = oracle.attend_unit(qo, K, V, T, good, 1)
+        check_rows(w, o[b, g * w.G:(g + 1) * w.G], ref, "%s invalid ids (%d,%d)" % (name, b, g))
