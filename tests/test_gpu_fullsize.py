@@ -134,3 +134,31 @@ def test_full_size_shared_selection_drift():
         ", ".join("(%d, %.1f, %d)" % x for x in diffs))
     del P
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_maximum_blocks_per_unit():
+    """The largest supported summary level: 32768 blocks per unit (1M tokens
+    at 32-token blocks), i.e. the full LDS bitmap, 128 scoring tasks per unit
+    and the general top-k with its keys in the workspace (more than 8192
+    candidates). Separate calls and the single-launch step, against the
+    oracle."""
+    w = CONFIGS[3].scaled(batch=1, hq=4, hkv=1, T=32768 * 32, needles=8)
+    assert w.nb == 32768
+    log("max blocks: generating and uploading %d tokens" % w.T)
+    P = Problem.make(w)
+    q = P.q()
+    summ = P.summaries()
+    ids_t, cnt_t = P.select(q, summ)
+    out = P.decode(q, ids_t, cnt_t)
+    ids2_t, cnt2_t, out2_t, _ = P.decode_step(q, summ, (w.T - 1) // w.S)
+    torch.cuda.synchronize()
+    ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+    assert np.array_equal(cnt2_t.cpu().numpy(), cnt)
+    assert np.array_equal(ids2_t.cpu().numpy()[0, 0, :cnt[0, 0]], ids[0, 0, :cnt[0, 0]])
+    o1 = out.cpu().double().numpy()
+    assert np.array_equal(out2_t.cpu().double().numpy(), o1)
+    check_units(w, P, q, ids, cnt, [o1], [(0, 0)])
+    log("max blocks: %d selected of %d blocks" % (cnt[0, 0], w.nb))
+    del P
+    torch.cuda.empty_cache()
