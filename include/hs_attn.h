@@ -320,12 +320,14 @@ hs_status hs_select_blocks(const hs_select_params* p, const hs_kv_cache* kv,
  * fp32 softmax and accumulation. If A is empty, out[b][h] = 0.
  *   q            : dtype[batch][Hq][head_dim]
  *   scale        : logit scale; 0 means 1 / sqrt(head_dim)
- *   block_size   : S of the ids (any S >= 1; need not equal page_size)
+ *   block_size   : S of the ids (any S >= 1; need not equal page_size).
+ *                  S = 1: the ids are single tokens (e.g. the token_ids of
+ *                  hs_select_tokens), each looked up through the page table.
  *   out          : float32[batch][Hq][head_dim]
  * The same block_ids may be passed to the decode of every layer (shared
- * selection, [SparDA 3.4]); they are only read. Ids of one unit must be
- * distinct (hs_select_blocks guarantees it); an id listed twice is attended
- * twice.
+ * selection, [SparDA 3.4]); they are only read. Ids outside
+ * [0, ceil(T_b / S)) are skipped. Ids of one unit must be distinct
+ * (hs_select_blocks guarantees it); an id listed twice is attended twice.
  * workspace: device buffer of at least hs_decode_workspace_size() bytes,
  *   16-byte aligned and ZERO-FILLED before its first use. It starts with
  *   per-unit arrival counters (the last split of a unit to finish merges the
@@ -347,7 +349,9 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
  * fine->block_size and p->max_selected. block_ids and num_selected are
  * written as by hs_select_blocks, out as by hs_sparse_decode, and the results
  * are bitwise identical to the two calls on the same inputs. A two-level
- * selection launches its coarse level first, then one fused launch.
+ * selection launches its coarse level first, then one fused launch; id lists
+ * too long for the fused kernel's LDS, and a fine block size of 1, run as the
+ * separate launches instead (same results).
  * Inside the launch, a unit's attention starts as soon as that unit's
  * selection is done, while other units are still being scored.
  * workspace: device buffer of at least hs_select_decode_workspace_size()
