@@ -812,8 +812,8 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
 }
 
 // Window and caller-forced blocks into the bitmap, then the bitmap as
-// ascending ids: to `list` (LDS) and/or to `gids` / `*gcnt` (global), either
-// may be null. Wave w emits its quarter of the bitmap words, 64 words per
+// ascending ids: to `list` (LDS, out_cap + kWave entries, the last kWave a
+// scratch area) and, if not null, to `gids` / `*gcnt` (global). Wave w emits its quarter of the bitmap words, 64 words per
 // round: lane l takes one word, a wave prefix sum of the words' popcounts
 // gives each its first position, and the lane writes its set bits in order.
 // Returns the count in every thread; the list is complete when it returns.
@@ -851,25 +851,31 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const U
     pos += w2 < wave ? t : 0u;
     total += t;
   }
+  // The bit loop has a wave-uniform trip count (the wave's largest popcount)
+  // and no branch: a lane without a bit left, or past the capacity, writes
+  // its trash slot list[cap + lane]. The global copy follows, coalesced.
   const uint32_t cap = (uint32_t)p.out_cap;
+  const uint32_t trash = cap + (uint32_t)lane;
   for (int wb = w_lo; wb < w_hi; wb += kWave) {  // wave-uniform: 64 words per round
     const int w = wb + lane;
     uint32_t x = w < w_hi ? bitmap[w] : 0u;
     const uint32_t c = (uint32_t)__popc(x);
     const uint32_t incl = wave_incl_scan(c);
     uint32_t at = pos + incl - c;
-    for (; x != 0u; x &= x - 1u, ++at) {  // this lane's set bits, ascending
-      if (at < cap) {
-        const int id = w * 32 + __builtin_ctz(x);
-        if (list) list[at] = id;
-        if (gids) gids[at] = id;
-      }
+    const int iters = (int)wave_max_u(c);
+    for (int i = 0; i < iters; ++i) {
+      const bool has = x != 0u;
+      list[has && at < cap ? at : trash] = w * 32 + __builtin_ctz(x | 0x80000000u);
+      x &= x - 1u;
+      at += has ? 1u : 0u;
     }
     pos += (uint32_t)__shfl((int)incl, kWave - 1);
   }
   const int cnt = (int)min(total, cap);
   if (gcnt && tid == 0) *gcnt = cnt;
   __syncthreads();
+  if (gids)
+    for (int i = tid; i < cnt; i += kThreads) gids[i] = list[i];
   return cnt;
 }
 
@@ -877,6 +883,8 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const U
 // scores: top-k, window, ascending ids. ug = unit_geom(p, unit) (callers
 // compute it early so its loads overlap other work). dyn = dynamic LDS laid
 // out as [bitmap: out_blocks_max bits][keys: n_slots_max words, general path].
+// list: the ids in LDS (out_cap + kWave entries, never null); gids / gcnt:
+// their global copy and count, or null.
 __device__ __forceinline__ int select_from_scores(const SelectParams& p, int unit,
                                                   const UnitGeom& ug, TopkShared& sh,
                                                   uint32_t* dyn, int32_t* list, int32_t* gids,
