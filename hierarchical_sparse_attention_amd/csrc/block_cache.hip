@@ -19,6 +19,7 @@ namespace hs {
 namespace {
 
 constexpr int kCacheThreads = 1024;  // one slot (capacity <= 1024) and one sort pair per thread
+constexpr int kMaxClasses = 8;       // stamp classes taken one by one before sorting
 
 __device__ __forceinline__ uint32_t wg_excl_sum(uint32_t x, uint32_t* tot, uint32_t* total) {
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
@@ -54,6 +55,7 @@ __host__ __device__ inline int sort_size(int c) {
 __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
   extern __shared__ int32_t lds[];
   __shared__ uint32_t tot[kCacheThreads / kWave];
+  __shared__ uint32_t cls_min[kCacheThreads / kWave];
   const int M = p.max_selected, C = p.capacity, t = p.step;
   const int N = sort_size(C);
   int32_t* ids = lds;
@@ -109,8 +111,41 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
     if (sof[j] < 0) mj[r++] = j;
   __syncthreads();  // tot is reused
   wg_excl_sum(prev, tot, &n_prev);
-  // eviction order: bitonic sort of the keys, ascending (only if a miss needs it)
-  if (n_miss > 0) {
+  // Eviction order. The misses usually fit in the few oldest stamp classes:
+  // classes are taken one at a time (the workgroup's smallest remaining
+  // stamp, then a prefix sum in slot order, slot s being thread s), which is
+  // exactly the start of the (stamp, slot) order. Past kMaxClasses classes
+  // the keys are sorted instead and the order continues from there.
+  uint32_t base = 0;  // misses placed so far
+  {
+    const uint64_t mykey = tid < N ? key[tid] : ~0ull;
+    const bool elig = mykey != ~0ull;
+    const uint32_t myst = (uint32_t)(mykey >> 32);  // stamp + 1
+    uint32_t floor_st = 0;                          // classes below it are taken
+    for (int cls = 0; base < n_miss && cls < kMaxClasses; ++cls) {  // uniform
+      uint32_t v = elig && myst >= floor_st ? myst : 0xFFFFFFFFu;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
+      if ((tid & (kWave - 1)) == 0) cls_min[tid / kWave] = v;
+      __syncthreads();
+      uint32_t m = 0xFFFFFFFFu;
+      for (int w = 0; w < kCacheThreads / kWave; ++w) m = min(m, cls_min[w]);
+      if (m == 0xFFFFFFFFu) break;  // no eligible slot left (uniform)
+      const bool in = elig && myst == m;
+      uint32_t n_in;
+      const uint32_t r = wg_excl_sum(in ? 1u : 0u, tot, &n_in);
+      if (in && base + r < n_miss) {
+        const int j = mj[base + r];
+        sof[j] = tid;
+        sblk[tid] = ids[j];
+        sst[tid] = t;
+      }
+      base += min(n_in, n_miss - base);
+      floor_st = m + 1;
+      __syncthreads();  // cls_min and tot are rewritten by the next class
+    }
+  }
+  if (base < n_miss) {  // uniform: sort the keys for the rest of the order
     for (int k = 2; k <= N; k <<= 1)
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < N; i += kCacheThreads) {
@@ -127,8 +162,8 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_update(CacheParams p) {
         __syncthreads();
       }
   }
-  // miss number q takes the q-th slot of the order
-  for (int q = tid; q < (int)n_miss; q += kCacheThreads) {
+  // miss number q takes the q-th slot of the order (the first `base` are placed)
+  for (int q = (int)base + tid; q < (int)n_miss; q += kCacheThreads) {
     const int s = (int)(uint32_t)key[q];
     const int j = mj[q];
     sof[j] = s;
