@@ -97,3 +97,16 @@ def test_block_cache_on_selections_of_the_pipeline():
     ov = run_and_check(sels, w.units, 4 * ms, ms, "pipeline")
     log("pipeline: overlap of consecutive selections min %.2f mean %.2f max %.2f" %
         (min(ov), float(np.mean(ov)), max(ov)))
+
+
+def test_block_cache_many_stamp_classes():
+    """Evictions that span more stamp classes than the kernel takes one by one
+    (it sorts the rest): one new block per step fills 32 slots with 32
+    distinct stamps, then a step misses 20 blocks at once."""
+    units, cap, ms = 2, 32, 24
+    sels = []
+    for t in range(32):
+        sels.append([[t], [100 + t]])          # one new block per step and unit
+    sels.append([list(range(200, 220)), list(range(300, 320))])  # 20 misses each
+    sels.append([[5] + list(range(200, 210)), list(range(300, 305))])  # ascending, as selected
+    run_and_check(sels, units, cap, ms, "many classes")
