@@ -764,11 +764,19 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
       const int nbins = 1 << db;
       for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
       __syncthreads();
-      for (int c = tid; c < n; c += kThreads) {
-        const uint32_t k = key_of(c);
-        if (k == 0) continue;
-        if (hi < 32 && (k >> hi) != (prefix >> hi)) continue;
-        atomicAdd(&sh.hist[hist_slot((k >> shift) & (uint32_t)(nbins - 1))], 1u);
+      // branch-free: a key outside the current prefix (or absent) counts in
+      // the lane's dummy bin; four keys per iteration
+      const uint32_t hmask = (uint32_t)((uint64_t)0xFFFFFFFFu << hi);  // bits at and above hi
+      const uint32_t dummy = kBins + (tid & (kWave - 1));
+      for (int c = tid; c < n; c += 4 * kThreads) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k4[i] = c + i * kThreads < n ? key_of(c + i * kThreads) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool in = k4[i] != 0u && ((k4[i] ^ prefix) & hmask) == 0u;
+          atomicAdd(&sh.hist[in ? hist_slot((k4[i] >> shift) & (uint32_t)(nbins - 1)) : dummy], 1u);
+        }
       }
       __syncthreads();
       take_digit(sh, nbins, shift, prefix, remaining);
