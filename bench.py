@@ -308,7 +308,7 @@ def main():
         log("decode loop: %.4f ms per step (append %.4f ms)" % (loop["ms_per_step"],
                                                                   loop["append_ms"]))
 
-    sched = tokens = cache = None
+    sched = tokens = cache = shared = None
     if not args.headline_only:
         sched = schedule_timing(w, copies, stream, args.event_steps)
         log("ratio %.2f + reserve set: %.4f ms per call, %.0f GB/s" % (
@@ -319,6 +319,10 @@ def main():
         cache = block_cache_timing(w, stream, args.event_steps)
         log("block cache update: %.4f ms per call (%d slots)" % (cache["ms_per_call"],
                                                                  cache["capacity"]))
+        shared = shared_selection_timing(stream, args.event_steps)
+        log("8 layers, shared selection: %.4f ms per token (%.0f GB/s); own selection per "
+            "layer: %.4f ms" % (shared["shared"]["ms_per_token"], shared["shared"]["GBps"],
+                                shared["per_layer"]["ms_per_token"]))
 
     # ----------------------------------------------------- CPU baseline
     cpu = None
@@ -362,6 +366,7 @@ def main():
         "warm_ms_per_step_single_copy": warm_ms,
         "decode_loop": loop,
         "block_cache": cache,
+        "shared_selection": shared,
         "token_stage": tokens,
         "ratio_and_reserve": sched,
         "cpu_baseline": cpu,
@@ -599,6 +604,109 @@ def block_cache_timing(w, stream, reps, steps=16, keep=0.85):
     return {"capacity": 4 * ms, "units": units, "steps": steps, "ms_per_call": ms_call,
             "mean_overlap": float(1.0 - st[:, :, 2].sum() / st[:, :, :2].sum()),
             "miss_rate": float(st[:, :, 1].sum() / st[:, :, :2].sum())}
+
+
+def shared_selection_timing(stream, reps):
+    """The 8-layer shared-selection workload (16 sequences of 64K tokens, GQA
+    32/8, d 128, bf16, mean summaries over 64-token pages, k 102, W 512, a
+    seeded page permutation), one decode token through all 8 layers, each
+    layer's K/V in its own pools. Shared: layer 0 runs hs_decode_step (refresh,
+    selection, attention) and layers 1-7 run hs_sparse_decode over the same
+    ids (SparDA section 3.3). Per layer, for contrast: every layer runs
+    hs_decode_step on its own summaries. Each variant is one captured graph,
+    timed with events."""
+    import numpy as np
+    import torch
+
+    import hierarchical_sparse_attention_amd as hs
+    from synth import device as sdev
+    from synth.workloads import CONFIGS
+
+    w = CONFIGS[5]
+    esize = 2 if w.dtype == "bf16" else 4
+    t = time.time()
+    pt = sdev.page_table_tensor(w)
+    sl = sdev.seq_lens_tensor(w)
+    cap = w.max_selected
+    last_block = (w.T - 1) // w.S
+    layers = []
+    for layer in range(w.layers):
+        kp, vp = sdev.make_pools(w, layer)
+        kv = hs.KVCache(kp, vp, pt, sl, w.T)
+        fine = hs.Summaries.empty(kv, w.kind, w.S)
+        L = dict(kv=kv, fine=fine, q=sdev.q_tensor(w, layer, 0),
+                 ids=torch.zeros((w.batch, w.hkv, cap), dtype=torch.int32, device="cuda"),
+                 cnt=torch.zeros((w.batch, w.hkv), dtype=torch.int32, device="cuda"),
+                 out=torch.zeros((w.batch, w.hq, w.d), dtype=torch.float32, device="cuda"),
+                 ws_f=hs.workspace(hs.hs_select_decode_workspace_size(
+                     kv, fine, w.hq, w.top_k, w.window, cap), "cuda"),
+                 ws_d=hs.workspace(hs.hs_decode_workspace_size(kv, w.hq, w.S, cap), "cuda"))
+        layers.append(L)
+    torch.cuda.synchronize()  # pools filled on torch's stream before the builds on `stream`
+    for L in layers:
+        hs.hs_build_summaries(L["kv"], L["fine"], 0, stream=stream)
+    torch.cuda.synchronize()
+    log("shared selection: %d layers on device in %.1f s" % (w.layers, time.time() - t))
+    L0 = layers[0]
+
+    def shared():
+        hs.hs_decode_step(L0["kv"], L0["q"], L0["fine"], w.top_k, w.window, last_block,
+                          L0["ids"], L0["cnt"], L0["out"], L0["ws_f"], stream=stream)
+        for L in layers[1:]:
+            hs.hs_sparse_decode(L["kv"], L["q"], w.S, L0["ids"], L0["cnt"], L["out"], L["ws_d"],
+                                stream=stream)
+
+    def own():
+        for L in layers:
+            hs.hs_decode_step(L["kv"], L["q"], L["fine"], w.top_k, w.window, last_block,
+                              L["ids"], L["cnt"], L["out"], L["ws_f"], stream=stream)
+
+    lens = w.seq_lens_array()
+
+    def decode_bytes(ids, cnt):
+        tok = sum(int(np.minimum(w.S, lens[b] - ids[b, g, :cnt[b, g]].astype(np.int64) * w.S).sum())
+                  for b in range(w.batch) for g in range(w.hkv))
+        return tok * w.d * esize * 2 + w.batch * w.hq * w.d * (esize + 4) + int(cnt.sum()) * 4
+
+    row = w.d * 4 if w.kind == "mean" else 2 * w.d * esize
+    select_bytes = w.units * w.nb * row + w.units * (w.S * w.d * esize + row)
+    res = {"workload": w.name, "layers": w.layers, "batch": w.batch, "q_heads": w.hq,
+           "kv_heads": w.hkv, "context": w.T, "block": w.S, "top_k": w.top_k,
+           "window": w.window, "page_table": "seeded permutation"}
+    for name, body in (("shared", shared), ("per_layer", own)):
+        with torch.cuda.stream(stream):
+            body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            body()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            g.replay()
+            for e0, e1 in evs:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        del g
+        if name == "shared":
+            b0 = decode_bytes(L0["ids"].cpu().numpy(), L0["cnt"].cpu().numpy())
+            nbytes = select_bytes + w.layers * b0
+            mean_sel = float(L0["cnt"].float().mean())
+        else:
+            nbytes = sum(select_bytes + decode_bytes(L["ids"].cpu().numpy(), L["cnt"].cpu().numpy())
+                         for L in layers)
+            mean_sel = float(np.mean([float(L["cnt"].float().mean()) for L in layers]))
+        res[name] = {"ms_per_token": ms, "query_heads_per_s": w.batch * w.hq / (ms * 1e-3),
+                     "bytes_per_token": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mean_selected": mean_sel}
+    del layers, L0
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, seconds):

@@ -161,7 +161,7 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
   if (block_size < 1 || max_selected < 1) return HS_ERR_INVALID_ARG;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->G = G;
-  L->n_splits = hs::decode_splits(L->units, max_selected);
+  L->n_splits = hs::decode_splits(L->units, max_selected, block_size);
   L->off_cnt = 0;
   L->off_o = align_up(sizeof(int32_t) * hs::kCounterStride * L->units);
   L->off_ml = align_up(L->off_o + sizeof(float) * L->units * L->n_splits * G * kv->head_dim);

@@ -6,7 +6,8 @@
 namespace hs {
 namespace {
 
-constexpr int kTargetTasks = 256;  // compute units of the GPU: about one split task each
+constexpr int kTargetTasks = 256;         // compute units of the GPU: about one split task each
+constexpr int64_t kLongSplit = 2048;      // tokens per split (full selection) that double the splits
 
 // One split task: the unit's count is read, its run of ids is copied into LDS
 // (written by an earlier launch, so plain loads), then attention and merge.
@@ -46,8 +47,9 @@ hipError_t launch_bf16(const DecodeParams& p, dim3 grid, size_t lds, hipStream_t
 
 }  // namespace
 
-int decode_splits(int64_t units, int32_t max_selected) {
+int decode_splits(int64_t units, int32_t max_selected, int32_t block_size) {
   int64_t ns = (kTargetTasks + units - 1) / units;
+  if ((int64_t)max_selected * block_size >= kLongSplit * ns) ns = (2 * kTargetTasks + units - 1) / units;
   if (ns > max_selected) ns = max_selected;
   if (ns > kMaxSplits) ns = kMaxSplits;
   return ns < 1 ? 1 : (int)ns;

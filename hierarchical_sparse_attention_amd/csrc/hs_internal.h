@@ -262,9 +262,11 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 constexpr int kMaxSplits = 128;
 // Split tasks per unit: enough to give every compute unit of the GPU about
-// one task (the work of a unit is its id list), at most one per selectable
+// one task (the work of a unit is its id list), two when a split would still
+// hold many tokens at the full selection (a second resident workgroup per
+// compute unit keeps more KV loads in flight), at most one per selectable
 // block and at most kMaxSplits.
-int decode_splits(int64_t units, int32_t max_selected);
+int decode_splits(int64_t units, int32_t max_selected, int32_t block_size);
 
 // Fused last selection level + decode of one layer (one persistent launch).
 struct StepParams {

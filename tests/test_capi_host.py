@@ -56,6 +56,31 @@ def sel_size(p, kv, fine, coarse=None):
     return st, n.value
 
 
+def test_decode_split_count_follows_the_work_per_split():
+    """Split tasks per unit, read off the decode workspace (partials o and
+    (m, l) per split): about 256 tasks in all, twice that when a split would
+    still hold 2048 or more tokens at the full selection."""
+    def dsize(kv, block_size, max_selected):
+        n = ctypes.c_size_t(0)
+        assert hs.lib().hs_decode_workspace_size(ctypes.byref(kv), 32, block_size, max_selected,
+                                                 ctypes.byref(n)) == hs.HS_OK
+        return n.value
+
+    per_split = 4 * (128 + 2) * 4  # G = 4 heads of (o[128], m, l) floats
+    # 16 x 8 = 128 units: 2 splits hold 111 tokens (block 1), 4 hold 111 blocks of 64
+    kv = kv_struct(batch=16, page_size=64, max_pages=1024, num_phys_pages=16 * 1024,
+                   max_seq_len=65536)
+    assert dsize(kv, 64, 111) - dsize(kv, 1, 111) == 128 * 2 * per_split
+    # 32 units at 145 blocks of 32 tokens: 8 splits of about 580 tokens stay 8
+    # (doubling would give 16 splits)
+    kv = kv_struct()
+    assert dsize(kv, 32, 145) - dsize(kv, 1, 145) == 0
+    # 256 units: one split of 73 x 64 tokens becomes two
+    kv = kv_struct(batch=8, num_kv_heads=32, page_size=64, max_pages=512,
+                   num_phys_pages=8 * 512, max_seq_len=32768)
+    assert dsize(kv, 64, 73) - dsize(kv, 1, 73) == 256 * 1 * (128 + 2) * 4
+
+
 def test_select_workspace_size_layout():
     p = hs.hs_select_params(32, 128, 512, 0, 145)
     st, n = sel_size(p, kv_struct(), summ())
