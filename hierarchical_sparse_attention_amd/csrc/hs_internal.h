@@ -69,6 +69,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Score stored for a candidate slot that holds no block: the all-ones NaN,
+// whose key is 0, the key of "no candidate".
+constexpr uint32_t kAbsentScore = 0xFFFFFFFFu;
+
 // ------------------------------------------------------ cross-lane reduction
 // Sum over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32, 64}); every
 // lane of a group ends with the group's sum. Within a 16-lane DPP row the

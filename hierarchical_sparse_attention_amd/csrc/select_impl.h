@@ -712,7 +712,7 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = cb + u * kThreads + tid;
-      const uint32_t k = c < n && slots.block_of(c) >= 0 ? order_key(v[u]) : 0u;
+      const uint32_t k = c < n ? order_key(v[u]) : 0u;  // 0 for kAbsentScore slots
       if (lds_keys && c < n) sk[c] = k;
       if (k) {
         ++cnt;
@@ -741,7 +741,7 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
   }
   auto key_of = [&](int c) -> uint32_t {
     if (lds_keys) return sk[c];
-    return slots.block_of(c) >= 0 ? order_key(published(&sc[c])) : 0u;
+    return order_key(published(&sc[c]));
   };
   const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
   if (k_eff == 0) return;
@@ -788,34 +788,47 @@ __device__ __forceinline__ void topk_general(const SelectParams& p, int unit, co
   // 3. mark kept blocks; thread t scans candidates [t*per, (t+1)*per) in order
   const int per = (n + kThreads - 1) / kThreads;
   const int c0 = tid * per, c1 = min(c0 + per, n);
+  // the first two coarse entries of the thread's run, loaded before the tie
+  // count so that their latency overlaps it
+  const bool two = slots.gamma != nullptr;
+  int gi = two ? c0 / slots.ratio : 0, r = two ? c0 - gi * slots.ratio : 0;
+  const int gi0 = gi;
+  const int pre0 = two && gi0 < slots.gcnt ? slots.gamma[gi0] : -1;
+  const int pre1 = two && gi0 + 1 < slots.gcnt ? slots.gamma[gi0 + 1] : -1;
   uint32_t ties = 0;
   if (!keep_all)
     for (int c = c0; c < c1; ++c) ties += key_of(c) == thr ? 1u : 0u;
   uint32_t tot;
   uint32_t rank = block_excl_scan(ties, &tot, sh);
   // consecutive candidates share their coarse entry (ratio slots each): its
-  // id is loaded once per entry instead of once per candidate
-  int last_gi = -1, last_base = 0;
+  // id is loaded once per entry, and the entry and the offset in it advance
+  // with the candidate instead of being divided out of it
+  int last_gi = -1, last_base = -1;
   for (int c = c0; c < c1; ++c) {
     const uint32_t k = key_of(c);
-    if (k == 0) continue;
-    bool keep = keep_all || k > thr;
-    if (!keep && k == thr) keep = rank++ < ties_keep;
-    if (!keep) continue;
-    int beta;
-    if (slots.gamma == nullptr) {
-      beta = c < slots.nb ? c : -1;
-    } else {
-      const int gi = c / slots.ratio;
-      if (gi != last_gi) {
-        last_gi = gi;
-        const int gg = gi < slots.gcnt ? slots.gamma[gi] : -1;
-        last_base = gg >= 0 ? gg * slots.ratio : -1;
+    bool keep = k != 0u && (keep_all || k > thr);
+    if (k != 0u && !keep && k == thr) keep = rank++ < ties_keep;
+    if (keep) {
+      int beta;
+      if (!two) {
+        beta = c < slots.nb ? c : -1;
+      } else {
+        if (gi != last_gi) {
+          last_gi = gi;
+          const int gg = gi == gi0       ? pre0
+                         : gi == gi0 + 1 ? pre1
+                                         : (gi < slots.gcnt ? slots.gamma[gi] : -1);
+          last_base = gg >= 0 ? gg * slots.ratio : -1;
+        }
+        beta = last_base < 0 ? -1 : last_base + r;
+        beta = beta < slots.nb ? beta : -1;
       }
-      beta = last_base < 0 ? -1 : last_base + c % slots.ratio;
-      beta = beta < slots.nb ? beta : -1;
+      if (beta >= 0) mark(bitmap, beta);
     }
-    if (beta >= 0) mark(bitmap, beta);
+    if (two && ++r == slots.ratio) {
+      r = 0;
+      ++gi;
+    }
   }
 }
 
@@ -847,8 +860,28 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const U
   __syncthreads();
   const int wpw = (words + kWaves - 1) / kWaves;  // words of each wave
   const int w_lo = wave * wpw, w_hi = min(w_lo + wpw, words);
-  uint32_t ones = 0;
-  for (int w = w_lo + lane; w < w_hi; w += kWave) ones += __popc(bitmap[w]);
+  // The wave's non-zero words (index, bits) are compacted, in order, into its
+  // share of sh.xpose (free once the top-k is done), so the bit loop below
+  // runs over them only: a sparse bitmap (a token level marks ~1.5 K bits of
+  // 131 K) would otherwise cost a round per 64 words whatever they hold.
+  constexpr int kScrWords = kThreads * kRegKeys / kWaves / 2;  // pairs per wave
+  uint32_t* scr_idx = reinterpret_cast<uint32_t*>(sh.xpose) + wave * 2 * kScrWords;
+  uint32_t* scr_bits = scr_idx + kScrWords;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t ones = 0, nz = 0;  // nz: the wave's non-zero words so far (uniform)
+  for (int wb = w_lo; wb < w_hi; wb += kWave) {  // wave-uniform
+    const int w = wb + lane;
+    const uint32_t x = w < w_hi ? bitmap[w] : 0u;
+    ones += __popc(x);
+    const uint64_t m = __ballot(x != 0u);
+    const uint32_t at = nz + (uint32_t)__popcll(m & below);
+    if (x != 0u && at < (uint32_t)kScrWords) {
+      scr_idx[at] = (uint32_t)w;
+      scr_bits[at] = x;
+    }
+    nz += (uint32_t)__popcll(m);
+  }
+  const bool compact = nz <= (uint32_t)kScrWords;  // else the full scan below
   ones = wave_sum_u(ones);
   if (lane == 0) sh.wave_tot[wave] = ones;
   __syncthreads();
@@ -864,9 +897,18 @@ __device__ __forceinline__ int emit_ids(const SelectParams& p, int unit, const U
   // its trash slot list[cap + lane]. The global copy follows, coalesced.
   const uint32_t cap = (uint32_t)p.out_cap;
   const uint32_t trash = cap + (uint32_t)lane;
-  for (int wb = w_lo; wb < w_hi; wb += kWave) {  // wave-uniform: 64 words per round
-    const int w = wb + lane;
-    uint32_t x = w < w_hi ? bitmap[w] : 0u;
+  const int r_end = compact ? (int)nz : w_hi - w_lo;
+  for (int rb = 0; rb < r_end; rb += kWave) {  // wave-uniform: 64 words per round
+    const int j = rb + lane;
+    int w;
+    uint32_t x;
+    if (compact) {
+      w = j < r_end ? (int)scr_idx[j] : 0;
+      x = j < r_end ? scr_bits[j] : 0u;
+    } else {
+      w = w_lo + j;
+      x = j < r_end ? bitmap[w] : 0u;
+    }
     const uint32_t c = (uint32_t)__popc(x);
     const uint32_t incl = wave_incl_scan(c);
     uint32_t at = pos + incl - c;
@@ -1049,13 +1091,16 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   // the chunk's largest key and largest ~key (its key range for the top-k)
   __syncthreads();
   const int c = c_wg + tid;
-  const bool ok = tid < kRowsPerWG && c < n_slots && ug.slots.block_of(c) >= 0;
+  const bool in = tid < kRowsPerWG && c < n_slots;
+  const bool ok = in && ug.slots.block_of(c) >= 0;
   uint32_t kx = 0, ki = 0;
   if (ok) {
     const float v = sh.stage[tid];
     publish(&p.scores[(int64_t)unit * p.n_slots_max + c], v);
     kx = order_key(v);
     ki = ~kx;
+  } else if (in) {  // a slot without a candidate: the all-ones NaN, whose key is 0 (absent)
+    publish(&p.scores[(int64_t)unit * p.n_slots_max + c], __uint_as_float(kAbsentScore));
   }
   kx = wave_max_u(kx);
   ki = wave_max_u(ki);

@@ -8,7 +8,9 @@ bit-exact except for near ties: a token may differ only if its oracle score
 lies within 1e-6 * max(|s_k|, sum_j sum_i |q_j,i k_t,i|) of the k-th kept
 score s_k, and never inside the window. Every top-k path of the token level is
 covered: the register path (up to 4096 candidates), the general path with
-keys in LDS (up to 8192) and with keys in the workspace (more).
+keys in LDS (up to 8192) and with keys in the workspace (more), and both forms
+of the id emission (compacted non-zero bitmap words, and the full scan of a
+dense bitmap).
 """
 import numpy as np
 import pytest
@@ -31,6 +33,10 @@ CASES = {
     "general-ws": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, top_k=257), 257, 128, 64),
     "f32-box": (C[1].scaled(hq=4, hkv=2, d=128, T=2500, kind="minmax", S=32, page_size=32,
                             top_k=7), 7, 40, 20),
+    # every block selected and a fifth of the 66000 tokens kept: nearly every
+    # 32-token word of the token bitmap is non-zero, more than the 512 words a
+    # wave compacts before emitting, so the emission scans the bitmap in full
+    "dense-scan": (C[3].scaled(batch=1, hq=4, hkv=1, T=66000, top_k=2063), 2063, 13200, 64),
 }
 _P = {}
 
