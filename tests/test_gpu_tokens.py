@@ -33,6 +33,11 @@ CASES = {
     "general-ws": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, top_k=257), 257, 128, 64),
     "f32-box": (C[1].scaled(hq=4, hkv=2, d=128, T=2500, kind="minmax", S=32, page_size=32,
                             top_k=7), 7, 40, 20),
+    "d64-g8-pages": (C[3].scaled(batch=2, hq=16, hkv=2, d=64, T=3001, kind="mean", S=64,
+                                 page_size=16, top_k=5, window=100, needles=0,
+                                 random_pages=True, seq_lens=(3001, 1500)), 5, 100, 50),
+    "mha-g1": (C[2].scaled(batch=2, hq=4, hkv=4, T=4133, seq_lens=(4133, 2100), top_k=20),
+               20, 300, 64),
     # every block selected and a fifth of the 66000 tokens kept: nearly every
     # 32-token word of the token bitmap is non-zero, more than the 512 words a
     # wave compacts before emitting, so the emission scans the bitmap in full
@@ -96,7 +101,7 @@ def test_token_stage_matches_oracle(name):
         name, t_cnt.reshape(-1).tolist(), ties))
 
 
-@pytest.mark.parametrize("name", ["regs", "f32-box"])
+@pytest.mark.parametrize("name", ["regs", "f32-box", "d64-g8-pages", "mha-g1"])
 def test_token_list_attention_skips_invalid_ids(name):
     """hs_sparse_decode with block size 1 over caller-made token lists salted
     with -1, ids at or past T_b and huge ids: the invalid entries are skipped,
