@@ -57,8 +57,9 @@ def parse():
                          "runs: their launches would mix into the kernel averages)")
     ap.add_argument("--loop-steps", type=int, default=64,
                     help="steps of the timed decode loop (append + step); 0 skips it")
-    ap.add_argument("--mode", choices=["step", "copy"], default="step",
-                    help="copy: plain device-to-device copy of known size (counter calibration)")
+    ap.add_argument("--mode", choices=["step", "copy", "shared"], default="step",
+                    help="copy: plain device-to-device copy of known size (counter calibration); "
+                         "shared: only the 8-layer shared-selection figure (its kernel trace)")
     return ap.parse_args()
 
 
@@ -118,6 +119,14 @@ def main():
         sys.exit(2)
     if args.mode == "copy":
         copy_mode(args)
+        return
+    if args.mode == "shared":
+        import torch
+        torch.cuda.set_device(0)
+        res = shared_selection_timing(torch.cuda.Stream(), args.event_steps)
+        print(json.dumps({"mode": "shared", "figure": "shared_selection", "reps": args.event_steps,
+                          "config": {"workload": res["workload"]}, "shared_selection": res}),
+              flush=True)
         return
     import numpy as np
     import torch

@@ -55,12 +55,18 @@ def stats(args):
         lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))
-    lines += ["", "Benchmark line of the same run:", "",
-              "- ms_per_step (graph replays, %d steps): %.4f" % (bench["steps"],
-                                                                bench["ms_per_step"]),
-              "- value: %.0f %s" % (bench["value"], bench["unit"]),
-              "- per-call event times (ms): %s" % json.dumps(bench["per_call_ms"]),
-              "- roofline: %s" % json.dumps(bench["roofline"]), ""]
+    if "figure" in bench:  # bench.py --mode shared (one figure)
+        lines += ["", "Figure of the same run (%s, %d event-timed graph replays each):" % (
+            bench["figure"], bench["reps"]), ""]
+        lines += ["- %s: %s" % (k, json.dumps(v)) for k, v in bench[bench["figure"]].items()]
+        lines.append("")
+    else:
+        lines += ["", "Benchmark line of the same run:", "",
+                  "- ms_per_step (graph replays, %d steps): %.4f" % (bench["steps"],
+                                                                    bench["ms_per_step"]),
+                  "- value: %.0f %s" % (bench["value"], bench["unit"]),
+                  "- per-call event times (ms): %s" % json.dumps(bench["per_call_ms"]),
+                  "- roofline: %s" % json.dumps(bench["roofline"]), ""]
     open(args.out_md, "w").write("\n".join(lines))
 
 
