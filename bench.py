@@ -332,6 +332,9 @@ def main():
         log("8 layers, shared selection: %.4f ms per token (%.0f GB/s); own selection per "
             "layer: %.4f ms" % (shared["shared"]["ms_per_token"], shared["shared"]["GBps"],
                                 shared["per_layer"]["ms_per_token"]))
+        log("selection drift over %d steps: |S_t minus S_t-1| min %d, mean %.1f, max %d" % (
+            shared["step_diff"]["steps"], shared["step_diff"]["min"], shared["step_diff"]["mean"],
+            shared["step_diff"]["max"]))
 
     # ----------------------------------------------------- CPU baseline
     cpu = None
@@ -713,6 +716,24 @@ def shared_selection_timing(stream, reps):
                      "bytes_per_token": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
                      "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "mean_selected": mean_sel}
+    # the selection's drift: layer-0 selections over the workload's decode steps
+    # (query q_t = 0.9 q_{t-1} + 0.44 n_t), |S_t minus S_t-1| per unit, untimed
+    ws_s = hs.workspace(hs.hs_select_workspace_size(L0["kv"], L0["fine"], w.hq, w.top_k,
+                                                    w.window, cap), "cuda")
+    ids_t = torch.zeros_like(L0["ids"])
+    cnt_t = torch.zeros_like(L0["cnt"])
+    prev, diffs = None, []
+    for t in range(w.steps):
+        hs.hs_select_blocks(L0["kv"], sdev.q_tensor(w, 0, t), L0["fine"], w.top_k, w.window,
+                            ids_t, cnt_t, ws_s)
+        ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+        cur = [set(ids[b, g, :cnt[b, g]].tolist()) for b in range(w.batch) for g in range(w.hkv)]
+        if prev is not None:
+            diffs.append([len(c - p_) for c, p_ in zip(cur, prev)])
+        prev = cur
+    d = np.array(diffs, dtype=np.float64)
+    res["step_diff"] = {"steps": w.steps, "min": int(d.min()), "mean": float(d.mean()),
+                        "max": int(d.max()), "mean_selected": float(np.mean([len(c) for c in prev]))}
     del layers, L0
     torch.cuda.empty_cache()
     return res
