@@ -15,6 +15,32 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectParams p, int list_of
                               reinterpret_cast<int32_t*>(dyn + list_off));
 }
 
+// One workgroup per unit: the pages of each selected block, in order, with the
+// number of each page's tokens below the unit's length (0: no token, e.g. an
+// absent entry, a page past T_b or an invalid page id).
+__global__ __launch_bounds__(kThreads) void k_tok_pages(SelectParams p) {
+  const int unit = blockIdx.x, b = unit / p.kv.num_kv_heads;
+  const UnitGeom ug = unit_geom(p, unit);
+  const int S = p.ratio, P = p.kv.page_size, ppb = p.tok_ppb;
+  int2* out = p.tok_pages + (int64_t)unit * p.gamma_cap * ppb;
+  for (int i = threadIdx.x; i < p.gamma_cap * ppb; i += kThreads) {
+    const int gi = i / ppb, j = i - gi * ppb;
+    int page = 0, lim = 0;
+    const int gg = gi < ug.slots.gcnt ? ug.slots.gamma[gi] : -1;
+    if (gg >= 0) {
+      const int64_t t0 = (int64_t)gg * S + (int64_t)j * P;  // first token of the page
+      if (t0 < ug.nb) {
+        const int pg = p.kv.page_table[(int64_t)b * p.kv.max_pages + (int)(t0 / P)];
+        if ((unsigned)pg < (unsigned)p.kv.num_phys_pages) {
+          page = pg;
+          lim = (int)min((int64_t)P, (int64_t)ug.nb - t0);
+        }
+      }
+    }
+    out[i] = make_int2(page, lim);
+  }
+}
+
 template <typename TE, int D, int KIND>
 hipError_t launch_g(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
   switch (p.G) {
@@ -44,6 +70,11 @@ size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max) {
 
 size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap) {
   return select_lds_bytes(out_blocks_max, n_slots_max) + sizeof(uint32_t) * ((size_t)out_cap + kWave);
+}
+
+hipError_t launch_tok_pages(const SelectParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_tok_pages, dim3(p.kv.batch * p.kv.num_kv_heads), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {

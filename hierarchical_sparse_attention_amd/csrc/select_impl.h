@@ -980,6 +980,10 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   const int c_begin = c_wg + wave * kRowsPerWave;
   const int li = lane % LPR, rg = lane / LPR;
   static_assert(kRowsPerWG <= kThreads, "at most one staged score per thread");
+  if constexpr (kTok) {  // a staged row that holds no token keeps the absent score
+    if (tid < kRowsPerWG) sh.stage[tid] = __uint_as_float(kAbsentScore);
+    __syncthreads();
+  }
 
   // the unit's G query heads folded into per-element coefficients
   float coef[EPS];
@@ -1036,13 +1040,28 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = cb + u * RPW + rg;
-        const int beta = c < c_end ? ug.slots.block_of(c) : -1;
-        cs[u] = beta >= 0 ? c : -1;
         if constexpr (kTok) {
-          const int64_t off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
+          int64_t off = -1;
+          if (p.tok_pages != nullptr) {
+            // the block's pages were resolved by launch_tok_pages: one load
+            // stands between the slot and its K row instead of two
+            if (c < c_end) {
+              const int gi = c / p.ratio, rr = c - gi * p.ratio, P = kv.page_size;
+              const int2 e = p.tok_pages[((int64_t)unit * p.gamma_cap + gi) * p.tok_ppb + rr / P];
+              if (rr % P < e.y)
+                off = (((int64_t)e.x * kv.num_kv_heads + g) * P + rr % P) *
+                      (int64_t)kv.head_dim * kv.elem_bytes;
+            }
+          } else {
+            const int beta = c < c_end ? ug.slots.block_of(c) : -1;
+            off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
+          }
+          cs[u] = off >= 0 ? c : -1;
           r[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
                           : make_uint4(0, 0, 0, 0);
         } else {
+          const int beta = c < c_end ? ug.slots.block_of(c) : -1;
+          cs[u] = beta >= 0 ? c : -1;
           r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
                            : make_uint4(0, 0, 0, 0);
         }
@@ -1092,7 +1111,9 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   __syncthreads();
   const int c = c_wg + tid;
   const bool in = tid < kRowsPerWG && c < n_slots;
-  const bool ok = in && ug.slots.block_of(c) >= 0;
+  bool ok;
+  if constexpr (kTok) ok = in && __float_as_uint(sh.stage[tid]) != kAbsentScore;
+  else ok = in && ug.slots.block_of(c) >= 0;
   uint32_t kx = 0, ki = 0;
   if (ok) {
     const float v = sh.stage[tid];
