@@ -227,7 +227,9 @@ hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_n
  *   aligned and ZERO-FILLED before its first use; every call leaves its
  *   counters at zero. Requires k_pool. HS_ERR_UNSUPPORTED when the
  *   workgroup's LDS (a bitmap of max_seq_len bits, the candidates' keys and
- *   the id list) would exceed 64 KiB. */
+ *   the id list) would exceed 64 KiB. When block_size is a multiple of the
+ *   page size the call is two launches on the stream: one resolves the
+ *   selected blocks' pages into the workspace, the other selects. */
 hs_status hs_select_tokens_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
                                           int32_t block_size, int32_t max_selected,
                                           int32_t top_k_tokens, int32_t window_tokens,
