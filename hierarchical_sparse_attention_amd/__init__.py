@@ -22,14 +22,17 @@ LIB_PATH = os.path.join(_HERE, "libhs_attn.so")
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP = range(5)
 HS_F32, HS_BF16 = 0, 1
 HS_SUMMARY_MEAN, HS_SUMMARY_MINMAX = 0, 1
+HS_STEP_WAIT_EXPIRED = 1
+# byte offsets in a hs_select_decode / hs_decode_step workspace (hs_attn.h)
+STEP_STATUS_BYTE, STEP_SELECT_BYTE = 0, 256
 KIND = {"mean": HS_SUMMARY_MEAN, "minmax": HS_SUMMARY_MINMAX}
 
 # Names declared in include/hs_attn.h; the CPU tests check that each is exported.
 EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_summaries",
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
            "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_block_cache_update",
-           "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_status_string",
-           "hs_version")
+           "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_step_status",
+           "hs_status_string", "hs_version")
 
 
 class hs_block_cache(ctypes.Structure):
@@ -112,11 +115,12 @@ def lib() -> ctypes.CDLL:
                                        vp, i32, vp, sz, vp]
         L.hs_block_cache_update.argtypes = [P(hs_block_cache), i32, i32, vp, vp, i32, vp, vp, vp,
                                             vp]
+        L.hs_step_status.argtypes = [vp, sz, P(ctypes.c_int32), vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
                      "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step",
                      "hs_append_kv", "hs_block_cache_update",
-                     "hs_select_tokens_workspace_size", "hs_select_tokens"):
+                     "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_step_status"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -432,6 +436,15 @@ def hs_decode_step(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int, wi
                                 num_selected, out, workspace, coarse, top_k_coarse, scale, stream,
                                 top_k_ratio, forced)
     _check("hs_decode_step", lib().hs_decode_step(*args))
+
+
+def hs_step_status(workspace: torch.Tensor, stream=None) -> int:
+    """Status word of a hs_select_decode / hs_decode_step workspace: 0, or
+    HS_STEP_WAIT_EXPIRED (synchronises the stream)."""
+    v = ctypes.c_int32(0)
+    _check("hs_step_status", lib().hs_step_status(_ptr(workspace), workspace.numel(),
+                                                  ctypes.byref(v), _stream(stream)))
+    return v.value
 
 
 def hs_version() -> int:

@@ -171,11 +171,12 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
 
 hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
 
-// Workspace of hs_select_decode: [selection workspace][decode workspace].
+// Workspace of hs_select_decode: [control words][selection workspace][decode
+// workspace].
 struct StepLayout {
   SelectLayout sel;
   DecodeLayout dec;
-  size_t off_sel, off_dec, total;
+  size_t off_ctrl, off_sel, off_dec, total;
 };
 
 hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_summaries* fine,
@@ -186,8 +187,9 @@ hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_
   if (st != HS_OK) return st;
   const int64_t chunks = hs::step_chunks((int32_t)L->sel.fine_slots);
   if (L->sel.units * (chunks + L->dec.n_splits) > 0x7FFFFFFF) return HS_ERR_UNSUPPORTED;
-  L->off_sel = 0;
-  L->off_dec = align_up(L->sel.total);
+  L->off_ctrl = 0;
+  L->off_sel = align_up(hs::kCtrlBytes);
+  L->off_dec = align_up(L->off_sel + L->sel.total);
   L->total = align_up(L->off_dec + L->dec.total);
   return HS_OK;
 }
@@ -278,6 +280,7 @@ hs::DecodeParams decode_params(const hs_kv_cache* kv, const void* q, float scale
   p.part_ml = reinterpret_cast<float*>(ws + L.off_ml);
   p.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
   p.score_counters = nullptr;
+  p.score_chunks = 0;
   p.out = out;
   return p;
 }
@@ -564,11 +567,14 @@ hs_status select_decode(const hs_select_params* prm, const hs_kv_cache* kv, cons
     if (e != hipSuccess) return from_hip(e);
     return from_hip(hs::launch_decode(p.dec, s));
   }
-  p.dec.score_counters = p.sel.counters;
   p.units = (int32_t)L.sel.units;
   p.n_chunks = hs::step_chunks(p.sel.n_slots_max);
   p.total = p.units * (p.n_chunks + p.dec.n_splits);
   p.list_cap = p.sel.out_cap;
+  p.dec.score_counters = p.sel.counters;
+  p.dec.score_chunks = p.n_chunks;
+  p.ctrl = reinterpret_cast<int32_t*>(ws + L.off_ctrl);
+  p.wait_ticks = 0;  // set by launch_step from the device's wall-clock rate
   return from_hip(hs::launch_step(p, s));
 }
 
@@ -582,6 +588,20 @@ hs_status hs_select_decode(const hs_select_params* prm, const hs_kv_cache* kv, c
                            void* workspace, size_t workspace_bytes, void* stream) {
   return select_decode(prm, kv, q, fine, coarse, -1, scale, block_ids, num_selected, out,
                        workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+hs_status hs_step_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream) {
+  if (!workspace || !status) return HS_ERR_INVALID_ARG;
+  if (workspace_bytes < sizeof(int32_t)) return HS_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, static_cast<const int32_t*>(workspace) + hs::kCtrlStatus,
+                                sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return HS_ERR_HIP;
+  *status = v;
+  return HS_OK;
 }
 
 hs_status hs_decode_step(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,

@@ -114,8 +114,8 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit) {
 
 // Combine the waves' states (in sh) into the task's partial, publish it and
 // arrive on the unit's counter; the last of the n_splits tasks to arrive
-// merges (and, in the fused launch, clears the unit's scoring counter, which
-// every task of the unit has read by then).
+// merges (and, in the fused launch, takes the unit's scoring arrivals off its
+// scoring counter, which every task of the unit has read by then).
 template <int D, int G>
 __device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<D, G>& sh, int unit,
                                              int split) {
@@ -142,7 +142,12 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, SplitShared<
     }
   }
   if (!arrive_last(counter_of(p.counters, unit), p.n_splits, &sh.last)) return;
-  if (p.score_counters != nullptr && tid == 0) publish_i32(counter_of(p.score_counters, unit), 0);
+  // the scoring arrivals this call counted are taken off again (not stored as
+  // zero), so the counter is zero for the next call even if a wait expired
+  // before the last scoring task arrived
+  if (p.score_counters != nullptr && tid == 0)
+    __hip_atomic_fetch_add(counter_of(p.score_counters, unit), -p.score_chunks, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   merge_splits<D, G>(p, unit);
 }
 
@@ -243,6 +248,14 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
     valid = off >= 0;
     return valid ? off : row0;
   };
+  // byte offset of token t of a stage that may straddle pages, and whether
+  // its page is valid (a token on an absent page is masked like a token past
+  // the stage, and its lane reads row 0 of the sequence instead)
+  auto stage_row = [&](int t, bool& valid) {
+    const int64_t off = row_offset(kv, b, g, t);
+    valid = off >= 0;
+    return valid ? off : row0;
+  };
   auto issue = [&](int st, StageRegs<D>& R, int& len) {
     len = st_len[wave][st];
     if (len == 0) return;
@@ -251,18 +264,12 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int ti = min(16 * tau + r16, len - 1);
-      // (an absent page reads row 0 instead: results are then unspecified,
-      // but every access stays inside the pool)
       int64_t off;
-      if (tok_list) {
-        bool valid;
-        off = token_row((int)base + ti, valid);
-        R.ok |= (valid && 16 * tau + r16 < len ? 1u : 0u) << tau;
-      } else {
-        off = whole_page ? base + ti * row_bytes
-                         : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
-        R.ok |= (16 * tau + r16 < len ? 1u : 0u) << tau;
-      }
+      bool valid = true;
+      if (tok_list) off = token_row((int)base + ti, valid);
+      else if (whole_page) off = base + ti * row_bytes;  // the stage's page is valid
+      else off = stage_row((int)base + ti, valid);
+      R.ok |= (valid && 16 * tau + r16 < len ? 1u : 0u) << tau;
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         R.k[tau][c] = *reinterpret_cast<const uint4*>(kv.k_pool + off + (32 * c + 8 * grp) * EB);
@@ -271,13 +278,10 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
     for (int u = 0; u < NV; ++u) {
       const int ti = min(TPV * u + vt, len - 1);
       int64_t off;
-      if (tok_list) {
-        bool valid;
-        off = token_row((int)base + ti, valid);
-      } else {
-        off = whole_page ? base + ti * row_bytes
-                         : max(row_offset(kv, b, g, (int)base + ti), (int64_t)0);
-      }
+      bool valid;
+      if (tok_list) off = token_row((int)base + ti, valid);
+      else if (whole_page) off = base + ti * row_bytes;
+      else off = stage_row((int)base + ti, valid);
       R.v[u] = *reinterpret_cast<const uint4*>(kv.v_pool + off + vd * EB);
     }
   };

@@ -268,6 +268,7 @@ struct DecodeParams {
   float* part_ml;            // [units][n_splits][G][2]
   int32_t* counters;         // [units] split arrivals; zero between calls
   int32_t* score_counters;   // fused launch: [units] scoring arrivals to clear, else null
+  int32_t score_chunks;      // fused launch: scoring arrivals per unit
   float* out;                // [B][Hq][d]
 };
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
@@ -279,12 +280,19 @@ constexpr int kMaxSplits = 128;
 // block and at most kMaxSplits.
 int decode_splits(int64_t units, int32_t max_selected, int32_t block_size);
 
+// Control line of the fused launch at the start of its workspace (int32
+// index of the status word the host reads; the line is 256 bytes).
+constexpr int kCtrlStatus = 0;
+constexpr int kCtrlBytes = kCounterStride * 4;
+
 // Fused last selection level + decode of one layer (one persistent launch).
 struct StepParams {
   SelectParams sel;          // the last (or only) selection level
   DecodeParams dec;          // counts / out / workspace of the decode
   int32_t units, n_chunks, total;
   int32_t list_cap;          // LDS id list entries (= sel.out_cap)
+  int32_t* ctrl;             // control line (kCtrlStatus)
+  long long wait_ticks;      // bound of a wait, in wall-clock ticks (set by launch_step)
 };
 hipError_t launch_step(const StepParams& p, hipStream_t s);
 int step_chunks(int32_t n_slots_max);  // scoring tasks per unit

@@ -25,22 +25,26 @@
 // task merges and clears the unit's counters.
 //
 // Scheduling: a persistent grid of R workgroups, R = what the GPU holds at
-// once (occupancy x compute units, from the HIP occupancy query), so every
-// workgroup of the grid is resident together. Task t goes to workgroup
-// t % R, which runs its tasks in increasing t. A split task only waits for
-// scoring tasks, which have smaller t and never wait: each is either done or
-// being run by its resident workgroup, whose earlier tasks are scoring tasks
-// too, so every wait ends. The wait is still bounded (kMaxSpins polls): if
-// the counter never comes, the task goes on with whatever scores are in
-// memory (ids are range-checked, so every access stays in bounds) and the
-// kernel ends.
+// once (occupancy x compute units, from the HIP occupancy query), so that
+// normally every workgroup of the grid is resident together. Task t goes to
+// workgroup t % R, which runs its tasks in increasing t. A split task only
+// waits for scoring tasks, which have smaller t and never wait: each is done
+// or being run by its resident workgroup, whose earlier tasks are scoring
+// tasks too, so every wait ends. That needs the whole grid resident: when
+// another kernel holds part of the GPU, a workgroup whose scoring task waits
+// for a free slot can keep a split task waiting. The wait is therefore
+// bounded by wall-clock time; when it expires the task goes on with whatever
+// scores are in memory (ids are range-checked, so every access stays in
+// bounds), the kernel ends, and the workspace's status word records it for
+// the caller. (Handing tasks out through a shared ticket counter would make
+// every wait end whatever the residency, but its same-address atomics made
+// the 128K step about 9 us slower.)
 #include "decode_impl.h"
 #include "select_impl.h"
 
 namespace hs {
 namespace {
 
-constexpr int kMaxSpins = 1 << 21;       // polls of a scoring counter
 constexpr size_t kMaxDynLds = 48 << 10;  // bitmap + keys + id list
 
 template <int D, int G>
@@ -76,8 +80,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const UnitGeom ug = unit_geom(p.sel, unit);  // its loads overlap the wait
       if (threadIdx.x == 0) {
         const int32_t* cnt = counter_of(p.sel.counters, unit);
-        for (int i = 0; i < kMaxSpins && published_i32(cnt) < NC; ++i)
+        const long long t0 = wall_clock64();
+        for (int i = 0; published_i32(cnt) < NC; ++i) {
           __builtin_amdgcn_s_sleep(4);
+          if ((i & 63) == 63 && wall_clock64() - t0 > p.wait_ticks) {
+            publish_i32(p.ctrl + kCtrlStatus, HS_STEP_WAIT_EXPIRED);
+            break;
+          }
+        }
       }
       __syncthreads();
       const bool writer = split == 0;
@@ -105,11 +115,23 @@ hipError_t resident_workgroups(const void* k, size_t lds, int* n) {
   return *n > 0 ? hipSuccess : hipErrorInvalidConfiguration;
 }
 
+// Bound of a wait on another workgroup: a quarter of a second of the
+// device's wall clock (a scoring task takes microseconds).
+hipError_t wait_bound(long long* ticks) {
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  *ticks = (long long)(khz > 0 ? khz : 100000) * 250;
+  return hipSuccess;
+}
+
 template <typename TE, int D, int KIND, int G>
-hipError_t launch_one(const StepParams& p, size_t lds, int list_off, hipStream_t s) {
+hipError_t launch_one(StepParams p, size_t lds, int list_off, hipStream_t s) {
   const void* k = reinterpret_cast<const void*>(&k_step<TE, D, KIND, G>);
   int r = 0;
-  const hipError_t e = resident_workgroups(k, lds, &r);
+  hipError_t e = resident_workgroups(k, lds, &r);
+  if (e == hipSuccess) e = wait_bound(&p.wait_ticks);
   if (e != hipSuccess) return e;
   const dim3 grid(r < p.total ? r : p.total);
   hipLaunchKernelGGL((k_step<TE, D, KIND, G>), grid, dim3(256), lds, s, p, list_off);

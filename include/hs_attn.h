@@ -41,8 +41,11 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
  *     caller allocates and owns every buffer. The library allocates nothing,
- *     keeps no host state between calls and is reentrant (two calls may run
- *     at the same time if they do not share output or workspace buffers).
+ *     keeps no host state between calls and is reentrant: two calls may run
+ *     at the same time if they do not share output or workspace buffers
+ *     (hs_select_decode and hs_decode_step then report an expired wait in
+ *     their status word if the other call kept part of their launch from
+ *     running; see there).
  *   - Struct arguments are read only during the call.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t, passed as
  *     void*; NULL = the default stream). Outputs are valid once the stream
@@ -53,10 +56,12 @@
  *   - Device-side values that the host cannot see (seq_lens, page-table
  *     entries, block ids, counts) are range-checked in the kernels: a sequence
  *     length is clamped to [0, max_seq_len]; a page-table entry outside
- *     [0, num_phys_pages) makes its tokens count as absent; a block id outside
- *     [0, ceil(T_b / block_size)) is skipped; a count is clamped to
- *     [0, max_selected]. No such value can make a kernel read or write out
- *     of bounds.
+ *     [0, num_phys_pages) is never dereferenced: the attention, the token
+ *     selection and the summaries leave its tokens out (a summary row of a
+ *     block with such tokens is then unspecified, as is a mean over none);
+ *     a block id outside [0, ceil(T_b / block_size)) is skipped; a count is
+ *     clamped to [0, max_selected]. No such value can make a kernel read or
+ *     write out of bounds.
  *   - Indexing: B = batch, Hkv = num_kv_heads, Hq = num_q_heads,
  *     G = Hq / Hkv (query head h uses KV head h / G), d = head_dim,
  *     P = page_size, S = block size of a summary level, T_b = seq_lens[b].
@@ -72,7 +77,11 @@
 extern "C" {
 #endif
 
-#define HS_ATTN_VERSION 2
+#define HS_ATTN_VERSION 3
+
+/* Value of the status word of a fused-step workspace (hs_step_status) after
+ * a call in which a workgroup's bounded wait for another expired. */
+#define HS_STEP_WAIT_EXPIRED 1
 
 typedef enum {
   HS_OK = 0,
@@ -356,11 +365,27 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q,
  * separate launches instead (same results).
  * Inside the launch, a unit's attention starts as soon as that unit's
  * selection is done, while other units are still being scored.
+ * The launch is a persistent grid sized to what the GPU holds at once, and a
+ * unit's attention tasks wait for that unit's scoring tasks, which run on
+ * other workgroups of the grid. Those waits end when the whole grid is
+ * resident, as it is when the call has the GPU to itself. When another
+ * kernel (or another fused call) holds part of the GPU at the same time, a
+ * scoring task can be held back until then; every wait is therefore bounded
+ * by wall-clock time (a quarter of a second). If one expires, the call's
+ * outputs are not valid and the workspace's status word is set to
+ * HS_STEP_WAIT_EXPIRED (read it with hs_step_status): callers that run other
+ * kernels concurrently with this one should check it, or use
+ * hs_select_blocks and hs_sparse_decode, which never wait. A workspace that
+ * was not zero-filled, or that overlapping calls share, also sets it.
  * workspace: device buffer of at least hs_select_decode_workspace_size()
- *   bytes, 16-byte aligned and ZERO-FILLED before its first use; it holds
- *   the workspaces of both stages. Every call returns its counters to zero,
- *   so it can be reused by later calls on the same stream but must not be
- *   shared by calls that may run at the same time. */
+ *   bytes, 16-byte aligned and ZERO-FILLED before its first use; it holds a
+ *   256-byte control line (status word at byte 0), then the workspace of the
+ *   selection (from byte 256; the last selection level's per-unit arrival
+ *   counters first, one int32 per 256 bytes), then that of the attention.
+ *   Every call returns its counters to zero, so it can be reused by later
+ *   calls on the same stream but must not be shared by calls that may run at
+ *   the same time. The status word is only ever set, never cleared, by the
+ *   library. */
 hs_status hs_select_decode_workspace_size(const hs_select_params* p,
                                           const hs_kv_cache* kv,
                                           const hs_summaries* fine,
@@ -393,6 +418,15 @@ hs_status hs_decode_step(const hs_select_params* p, const hs_kv_cache* kv,
                          float scale, int32_t* block_ids,
                          int32_t* num_selected, float* out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Reads the status word of a workspace of hs_select_decode / hs_decode_step
+ * into *status (0, or HS_STEP_WAIT_EXPIRED once a call on the workspace had
+ * an expired wait; it stays set until the caller zero-fills the workspace
+ * again). Waits for `stream` to reach this point (a device-to-host copy of
+ * 4 bytes on it, then a stream synchronisation), so it is meant for checks
+ * and tests rather than for every step. workspace_bytes must be >= 4. */
+hs_status hs_step_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* hs_status_string(hs_status s);

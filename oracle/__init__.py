@@ -50,7 +50,6 @@ def lib():
             build(force=False)
         L = ctypes.CDLL(_LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        L.hso_widen.argtypes = [vp, i32, i64, vp]
         L.hso_gather_unit.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
         L.hso_gather_unit.restype = i32
         L.hso_summary_mean.argtypes = [vp, i32, i32, i32, vp]
@@ -64,7 +63,7 @@ def lib():
                                       i32, vp, vp, vp, vp]
         L.hso_select_unit.restype = i32
         L.hso_attend_unit.argtypes = [vp, i32, i32, vp, vp, i32, vp, i32, i32, dbl, vp]
-        for name in ("hso_widen", "hso_summary_mean", "hso_summary_minmax", "hso_scores_mean",
+        for name in ("hso_summary_mean", "hso_summary_minmax", "hso_scores_mean",
                      "hso_scores_minmax", "hso_window", "hso_attend_unit"):
             getattr(L, name).restype = None
         _lib = L
@@ -80,14 +79,6 @@ def _p(a: Optional[np.ndarray]):
 
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, np.float64)
-
-
-def widen(x: np.ndarray, dtype: int) -> np.ndarray:
-    """Exact float64 values of stored float32 (dtype F32) or bf16 bits (BF16)."""
-    x = np.ascontiguousarray(x, np.float32 if dtype == F32 else np.uint16)
-    out = np.empty(x.shape, np.float64)
-    lib().hso_widen(_p(x), dtype, x.size, _p(out))
-    return out
 
 
 def gather_unit(pool: np.ndarray, dtype: int, page_table: np.ndarray, b: int, g: int,

@@ -44,11 +44,6 @@ static double widen_one(const void* base, int dtype, size_t i) {
   return (double)f;
 }
 
-/* Exact double values of n stored elements. */
-void hso_widen(const void* src, int dtype, int64_t n, double* out) {
-  for (int64_t i = 0; i < n; ++i) out[i] = widen_one(src, dtype, (size_t)i);
-}
-
 /* Logical -> physical addressing of a paged cache ([SGL 2.2]: the page table
  * maps a logical block to its physical page; [HiSp 3.2]: a page holds its
  * tokens contiguously). Row t of unit (b, g) is

@@ -33,14 +33,17 @@ def seq_lens_tensor(w: Workload, device="cuda") -> torch.Tensor:
 
 
 def fill_pool(w: Workload, which: str, layer: int, pool: torch.Tensor,
-              page_table: np.ndarray) -> None:
+              page_table: np.ndarray, rows_of=None) -> None:
     """Write one layer's K or V of every unit into `pool` (device tensor
-    [num_phys][Hkv][P][d]) through `page_table` [B][max_pages]."""
+    [num_phys][Hkv][P][d]) through `page_table` [B][max_pages]. rows_of:
+    optional callable (which, layer, b) -> [Hkv][T][d] storage rows that
+    replaces the generator (a test that edits the generated rows)."""
     P, d, npg = w.page_size, w.d, w.max_pages
     pad = npg * P - w.T
     dev = pool.device
+    get = rows_of if rows_of is not None else w.kv_rows
     for b in range(w.batch):
-        rows = to_torch(w.kv_rows(which, layer, b), w.dtype).to(dev)  # [Hkv][T][d]
+        rows = to_torch(get(which, layer, b), w.dtype).to(dev)  # [Hkv][T][d]
         if pad:
             rows = torch.cat([rows, torch.zeros((w.hkv, pad, d), dtype=rows.dtype, device=dev)], 1)
         pages = rows.view(w.hkv, npg, P, d).permute(1, 0, 2, 3)      # [npg][Hkv][P][d]
@@ -49,12 +52,12 @@ def fill_pool(w: Workload, which: str, layer: int, pool: torch.Tensor,
         del rows, pages
 
 
-def make_pools(w: Workload, layer: int = 0, device="cuda"):
-    """(k_pool, v_pool) device tensors of one layer."""
+def make_pools(w: Workload, layer: int = 0, device="cuda", rows_of=None):
+    """(k_pool, v_pool) device tensors of one layer (rows_of: see fill_pool)."""
     shape = (w.num_phys_pages, w.hkv, w.page_size, w.d)
     pt = w.page_table()
     kp = torch.zeros(shape, dtype=TORCH_DTYPE[w.dtype], device=device)
     vp = torch.zeros(shape, dtype=TORCH_DTYPE[w.dtype], device=device)
-    fill_pool(w, "k", layer, kp, pt)
-    fill_pool(w, "v", layer, vp, pt)
+    fill_pool(w, "k", layer, kp, pt, rows_of)
+    fill_pool(w, "v", layer, vp, pt, rows_of)
     return kp, vp

@@ -19,7 +19,7 @@ import math
 import sys
 import time
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional
 
 import numpy as np
 import torch
@@ -49,17 +49,29 @@ class Problem:
     kvs: List[hs.KVCache] = field(default_factory=list)
     page_table: Optional[torch.Tensor] = None
     seq_lens: Optional[torch.Tensor] = None
+    rows_of: Optional[Callable] = None  # (which, layer, b) -> [Hkv][T][d], else the generator
 
     @staticmethod
-    def make(w: Workload, layers: int = 1) -> "Problem":
-        p = Problem(w=w, layers=layers)
+    def make(w: Workload, layers: int = 1, rows_of: Optional[Callable] = None) -> "Problem":
+        p = Problem(w=w, layers=layers, rows_of=rows_of)
         p.page_table = sdev.page_table_tensor(w)
         p.seq_lens = sdev.seq_lens_tensor(w)
         for layer in range(layers):
-            kp, vp = sdev.make_pools(w, layer)
+            kp, vp = sdev.make_pools(w, layer, rows_of=rows_of)
             p.kvs.append(hs.KVCache(kp, vp, p.page_table, p.seq_lens, w.T))
         torch.cuda.synchronize()
         return p
+
+    def unit_inputs(self, layer: int, b: int, g: int, step: int = 0):
+        """Oracle-side q [G][d], K and V rows [T][d] (float64) of one unit,
+        from the same rows the pools were filled with."""
+        if self.rows_of is None:
+            return unit_inputs(self.w, layer, b, g, step)
+        w = self.w
+        q = synth.widen(w.q(layer, step), w.dtype)[b, g * w.G:(g + 1) * w.G]
+        K = synth.widen(self.rows_of("k", layer, b)[g], w.dtype)
+        V = synth.widen(self.rows_of("v", layer, b)[g], w.dtype)
+        return q, K, V
 
     def q(self, layer=0, step=0) -> torch.Tensor:
         return sdev.q_tensor(self.w, layer, step)
@@ -160,25 +172,40 @@ def magnitudes(w: Workload, q, K, T) -> np.ndarray:
     return x @ np.abs(q).sum(axis=0)
 
 
+def paired_differences(got: List[int], ref: List[int], what: str):
+    """The GPU list and the oracle's must have the same size; returns the
+    pairs (dropped oracle id, extra GPU id), each side in ascending order.
+    Every difference is then one oracle id traded for one GPU id, and both
+    members of each pair are judged by the near-tie rule."""
+    assert len(got) == len(ref), "%s: %d ids, the oracle keeps %d" % (what, len(got), len(ref))
+    dropped = sorted(set(ref) - set(got))
+    extra = sorted(set(got) - set(ref))
+    assert len(dropped) == len(extra), what
+    return list(zip(dropped, extra))
+
+
 def check_ids(w: Workload, gpu_ids: np.ndarray, sel: oracle.UnitSelection, mags: np.ndarray,
               T: int, window=None, what="") -> int:
-    """Assert the near-tie rule; returns the number of tolerated differences."""
+    """Assert the near-tie rule; returns the number of tolerated differences
+    (pairs of one dropped oracle block and one extra GPU block)."""
     W = w.window if window is None else window
     g = gpu_ids.tolist()
     assert g == sorted(set(g)), "%s: ids not strictly ascending: %s" % (what, g[:20])
-    diff = set(g) ^ set(sel.ids.tolist())
-    if not diff:
+    pairs = paired_differences(g, sel.ids.tolist(), what)
+    if not pairs:
         return 0
     win = set(oracle.window_blocks(T, w.S, W).tolist())
     sk = sel.kth_score
-    for beta in diff:
-        assert beta not in win, "%s: window block %d missing" % (what, beta)
-        s = sel.fine_scores[beta] if 0 <= beta < len(sel.fine_scores) else float("nan")
-        assert not math.isnan(s), "%s: block %d was not a candidate" % (what, beta)
-        tol = TIE_RTOL * max(abs(sk), mags[beta])
-        assert abs(s - sk) <= tol, ("%s: block %d differs, score %.9g vs k-th %.9g (tol %.3g)"
-                                    % (what, beta, s, sk, tol))
-    return len(diff)
+    for pair in pairs:
+        for beta in pair:
+            assert beta not in win, "%s: window block %d differs" % (what, beta)
+            s = sel.fine_scores[beta] if 0 <= beta < len(sel.fine_scores) else float("nan")
+            assert not math.isnan(s), "%s: block %d was not a candidate" % (what, beta)
+            tol = TIE_RTOL * max(abs(sk), mags[beta])
+            assert abs(s - sk) <= tol, (
+                "%s: block %d (pair %s) differs, score %.9g vs k-th %.9g (tol %.3g)"
+                % (what, beta, pair, s, sk, tol))
+    return len(pairs)
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -27,7 +27,18 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert hs.hs_version() == 2
+    assert hs.hs_version() == 3
+
+
+def test_step_status_rejects_bad_arguments():
+    """hs_step_status validates before any HIP call: null pointers and a
+    workspace shorter than the status word."""
+    L = hs.lib()
+    v = ctypes.c_int32(7)
+    assert L.hs_step_status(None, 4096, ctypes.byref(v), None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_step_status(FAKE, 4096, None, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_step_status(FAKE, 3, ctypes.byref(v), None) == hs.HS_ERR_WORKSPACE
+    assert v.value == 7
 
 
 def test_status_strings():

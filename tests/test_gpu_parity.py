@@ -162,10 +162,12 @@ def test_fused_select_decode_equals_separate_calls(name):
         assert torch.equal(cnt_f, cnt_s), (name, call)
         assert torch.equal(ids_f, ids_s), (name, call)
         assert torch.equal(out_f, out_s), (name, call, float((out_f - out_s).abs().max()))
-    # the workspace starts with the selection's arrival counters (two levels,
-    # one 256-byte line per unit)
+    # the workspace starts with the control line (status word),
+    # then the selection's arrival counters (two levels, one 256-byte line
+    # per unit): all zero after a call
     units_n = P.w.batch * P.w.hkv
-    assert int(ws[:2 * 256 * units_n].view(torch.int32).abs().sum()) == 0, name
+    end = hs.STEP_SELECT_BYTE + 2 * 256 * units_n
+    assert int(ws[:end].view(torch.int32).abs().sum()) == 0, name
     log("%s fused == separate, 3 calls" % name)
 
 
@@ -313,3 +315,97 @@ def test_incremental_refresh_of_last_block():
     hs.hs_build_summaries(kv, full)
     torch.cuda.synchronize()
     assert torch.equal(inc.data, full.data)
+
+
+ABSENT = {
+    "bf16": C[3].scaled(batch=3, hq=8, hkv=2, T=3001, kind="mean", S=16, page_size=16,
+                        top_k=5, window=100, needles=0, seq_lens=(3001, 2000, 1500)),
+    "f32": C[1].scaled(batch=3, hq=4, hkv=2, d=128, T=3001, page_size=16,
+                       seq_lens=(3001, 2000, 1500)),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("S", [1, 16, 48, 64])
+def test_decode_skips_absent_pages(dtype, S):
+    """Page-table entries outside [0, num_phys_pages) (-1 and past the pool)
+    make their tokens absent: the decode attends over the selected tokens on
+    valid pages only, for block sizes that make a 32-token stage straddle
+    pages (page size 16) and for token lists. Sequence 2 has no valid page
+    at all, so its rows are 0."""
+    w = ABSENT[dtype]
+    key = ("absent", dtype)
+    if key not in _PROBLEMS:
+        _PROBLEMS[key] = Problem.make(w)
+    P = _PROBLEMS[key]
+    kv0 = P.kvs[0]
+    pt = w.page_table().copy()
+    rng = np.random.default_rng(5)
+    bad = rng.random(pt.shape) < 0.3
+    pt[bad & (rng.random(pt.shape) < 0.5)] = -1
+    pt[bad & (pt >= 0)] = w.num_phys_pages + 5
+    pt[2] = -1
+    kv = hs.KVCache(kv0.k_pool, kv0.v_pool, torch.from_numpy(pt).cuda(), kv0.seq_lens, w.T)
+    lens = w.seq_lens_array()
+    n_ids = 24 if S > 1 else 400
+    ids = np.full((w.batch, w.hkv, n_ids), -1, np.int32)
+    cnt = np.zeros((w.batch, w.hkv), np.int32)
+    for b, g in units(w):
+        T = int(lens[b])
+        nb = -(-T // S)
+        pick = np.sort(rng.choice(nb, size=min(n_ids, nb), replace=False)).astype(np.int32)
+        ids[b, g, :len(pick)] = pick
+        cnt[b, g] = len(pick)
+    ws = hs.workspace(hs.hs_decode_workspace_size(kv, w.hq, S, n_ids), "cuda")
+    out = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    hs.hs_sparse_decode(kv, P.q(), S, torch.from_numpy(ids).cuda(), torch.from_numpy(cnt).cuda(),
+                        out, ws)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    ref = np.zeros_like(o)
+    absent = 0
+    for b, g in units(w):
+        T = int(lens[b])
+        qo, K, V = unit_inputs(w, 0, b, g)
+        toks = [t for beta in ids[b, g, :cnt[b, g]] for t in range(beta * S, min(beta * S + S, T))]
+        ok = [t for t in toks if 0 <= pt[b, t // w.page_size] < w.num_phys_pages]
+        absent += len(toks) - len(ok)
+        ref[b, g * w.G:(g + 1) * w.G] = oracle.attend_unit(qo, K, V, T, np.array(ok, np.int32), 1)
+    assert np.all(o[2] == 0), "a sequence without valid pages must give zero rows"
+    err = check_rows(w, o, ref, "absent pages %s S=%d" % (dtype, S))
+    log("absent pages %s S=%d: %d absent tokens skipped, max row rel err %.3g" % (
+        dtype, S, absent, err))
+
+
+@pytest.mark.parametrize("name", ["c3s", "c1-ragged", "c4s"])
+def test_split_count_invariance(name):
+    """The same ids decoded through id rows of different capacity: the
+    capacity sets the number of split tasks per unit (hs_decode_workspace_size
+    grows with it), so the tokens are cut into different runs and merged in a
+    different order; both outputs match the oracle's attention over the ids."""
+    P = problem(name)
+    w = P.w
+    q = P.q()
+    summ = P.summaries()
+    ids_t, cnt_t = P.select(q, summ)
+    ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+    lens = w.seq_lens_array()
+    ref = np.zeros((w.batch, w.hq, w.d))
+    for b, g in units(w):
+        qo, K, V = unit_inputs(w, 0, b, g)
+        ref[b, g * w.G:(g + 1) * w.G] = oracle.attend_unit(qo, K, V, int(lens[b]),
+                                                           ids[b, g, :cnt[b, g]], w.S)
+    cap0 = ids.shape[-1]
+    # splits per unit: min(capacity, ceil(256 / units)), doubled once a split
+    # would hold >= 2048 tokens at full capacity; the largest capacity below
+    # crosses that threshold, the smallest caps the count at the ids' count
+    per = -(-256 // w.units)
+    big = max(cap0, -(-2048 * per // w.S)) + 1
+    sizes = set()
+    for cap in (int(cnt.max()), cap0, big):
+        wide = np.full((w.batch, w.hkv, cap), -1, np.int32)
+        wide[:, :, :min(cap, cap0)] = ids[:, :, :min(cap, cap0)]
+        sizes.add(hs.hs_decode_workspace_size(P.kvs[0], w.hq, w.S, cap))
+        out = P.decode(q, torch.from_numpy(wide).cuda(), cnt_t).cpu().double().numpy()
+        check_rows(w, out, ref, "%s capacity %d" % (name, cap))
+    assert len(sizes) > 1, "%s: capacities did not change the split count" % name
