@@ -32,7 +32,7 @@ EXPORTS = ("hs_select_workspace_size", "hs_decode_workspace_size", "hs_build_sum
            "hs_select_blocks", "hs_sparse_decode", "hs_select_decode_workspace_size",
            "hs_select_decode", "hs_decode_step", "hs_append_kv", "hs_block_cache_update",
            "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_step_status",
-           "hs_status_string", "hs_version")
+           "hs_decode_step_noalloc", "hs_status_string", "hs_version")
 
 
 class hs_block_cache(ctypes.Structure):
@@ -116,11 +116,15 @@ def lib() -> ctypes.CDLL:
         L.hs_block_cache_update.argtypes = [P(hs_block_cache), i32, i32, vp, vp, i32, vp, vp, vp,
                                             vp]
         L.hs_step_status.argtypes = [vp, sz, P(ctypes.c_int32), vp]
+        L.hs_decode_step_noalloc.argtypes = [P(hs_select_params), P(hs_kv_cache), vp,
+                                             P(hs_summaries), P(hs_summaries), i32,
+                                             ctypes.c_float, vp, vp, vp, vp]
         for name in ("hs_select_workspace_size", "hs_decode_workspace_size",
                      "hs_build_summaries", "hs_select_blocks", "hs_sparse_decode",
                      "hs_select_decode_workspace_size", "hs_select_decode", "hs_decode_step",
                      "hs_append_kv", "hs_block_cache_update",
-                     "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_step_status"):
+                     "hs_select_tokens_workspace_size", "hs_select_tokens", "hs_step_status",
+                     "hs_decode_step_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -445,6 +449,34 @@ def hs_step_status(workspace: torch.Tensor, stream=None) -> int:
     _check("hs_step_status", lib().hs_step_status(_ptr(workspace), workspace.numel(),
                                                   ctypes.byref(v), _stream(stream)))
     return v.value
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # HS_NOALLOC_SCRATCH_BYTES
+
+
+def hs_decode_step_noalloc(kv: KVCache, q: torch.Tensor, fine: Summaries, top_k: int,
+                           window: int, refresh_begin: int, block_ids: torch.Tensor,
+                           num_selected: torch.Tensor, out: torch.Tensor,
+                           coarse: Optional[Summaries] = None, top_k_coarse: int = 0,
+                           scale: float = 0.0, stream=None, top_k_ratio: float = 0.0,
+                           forced: Optional[torch.Tensor] = None) -> None:
+    """hs_decode_step with the library's own device array as its workspace
+    (no allocation by the library or here); calls that overlap on one GPU race."""
+    if block_ids.dtype != torch.int32 or num_selected.dtype != torch.int32:
+        raise ValueError("block_ids and num_selected must be int32")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    p = _sel_params(q.shape[1], top_k, window, top_k_coarse, block_ids.shape[-1], top_k_ratio,
+                    forced)
+    ks, fs = kv.struct(), fine.struct()
+    cs = coarse.struct() if coarse is not None else None
+    _check("hs_decode_step_noalloc",
+           lib().hs_decode_step_noalloc(ctypes.byref(p), ctypes.byref(ks), _ptr(q),
+                                        ctypes.byref(fs),
+                                        ctypes.byref(cs) if cs is not None else None,
+                                        int(refresh_begin), ctypes.c_float(scale),
+                                        _ptr(block_ids), _ptr(num_selected), _ptr(out),
+                                        _stream(stream)))
 
 
 def hs_version() -> int:

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "hs_internal.h"
 
@@ -613,6 +614,83 @@ hs_status hs_decode_step(const hs_select_params* prm, const hs_kv_cache* kv, con
   if (kv && (!kv->k_pool || !aligned16(kv->k_pool))) return HS_ERR_INVALID_ARG;
   return select_decode(prm, kv, q, fine, coarse, refresh_begin, scale, block_ids, num_selected,
                        out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ no-allocation decode step
+// hs_decode_step_noalloc runs hs_decode_step with its workspace in `scratch`,
+// a device array of this library. Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and kept in
+// scratch_dev[]; every use goes through that address.
+static __device__ __align__(256) uint8_t scratch[HS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+hs_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HS_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return HS_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return HS_OK;
+}
+
+// Zeroes [0, n0) and [off1, off1 + n1) bytes of `base` (multiples of 16): the
+// control line and arrival counters that a call needs at zero. A kernel, not
+// hipMemsetAsync, so that the call can be captured into a graph.
+__global__ void k_clear_counters(uint8_t* base, int64_t n0, int64_t off1, int64_t n1) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 16;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; i < n0 + n1;
+       i += stride) {
+    const int64_t at = i < n0 ? i : off1 + (i - n0);
+    *reinterpret_cast<uint4*>(base + at) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_decode_step_noalloc(const hs_select_params* prm, const hs_kv_cache* kv,
+                                 const void* q, const hs_summaries* fine,
+                                 const hs_summaries* coarse, int32_t refresh_begin, float scale,
+                                 int32_t* block_ids, int32_t* num_selected, float* out,
+                                 void* stream) {
+  // every argument is checked, and the size against the array's, before any HIP call
+  if (refresh_begin < 0) return HS_ERR_INVALID_ARG;
+  if (kv && (!kv->k_pool || !aligned16(kv->k_pool))) return HS_ERR_INVALID_ARG;
+  StepLayout L;
+  hs_status st = check_step(prm, kv, fine, coarse, &L);
+  if (st != HS_OK) return st;
+  if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
+  if (L.total > (size_t)HS_NOALLOC_SCRATCH_BYTES) return HS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != HS_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the control line and the selection's counters are contiguous at the
+  // start; the attention's counters start its part
+  const int64_t n0 = (int64_t)(L.off_sel + align_up(sizeof(int32_t) * hs::kCounterStride * 2 *
+                                                   L.sel.units));
+  const int64_t n1 = (int64_t)align_up(sizeof(int32_t) * hs::kCounterStride * L.dec.units);
+  hipLaunchKernelGGL(k_clear_counters, dim3(64), dim3(256), 0, s, static_cast<uint8_t*>(ws), n0,
+                     (int64_t)L.off_dec, n1);
+  if (hipGetLastError() != hipSuccess) return HS_ERR_HIP;
+  return select_decode(prm, kv, q, fine, coarse, refresh_begin, scale, block_ids, num_selected,
+                       out, ws, (size_t)HS_NOALLOC_SCRATCH_BYTES, s);
 }
 
 }  // extern "C"

@@ -419,6 +419,29 @@ hs_status hs_decode_step(const hs_select_params* p, const hs_kv_cache* kv,
                          int32_t* num_selected, float* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* hs_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, results and their bitwise
+ * equality with hs_build_summaries + hs_select_decode are those of
+ * hs_decode_step. The workspace is a device array of the library,
+ * HS_NOALLOC_SCRATCH_BYTES long, that each GPU the library runs on holds
+ * until the process ends; its device address is looked up on the first call
+ * on each device (HIP's symbol lookup, no allocation). Each call first
+ * zeroes the array's control line and arrival counters with a small kernel
+ * on `stream`, then runs the step. Calls on one GPU share the array: calls
+ * that overlap on one GPU (several streams, or threads) race and give wrong
+ * results. The status word of an expired wait (see hs_decode_step) is not
+ * readable for this variant; use it when the call has the GPU to itself.
+ * Returns HS_ERR_WORKSPACE, before any HIP call, when the step's workspace
+ * (hs_select_decode_workspace_size) would exceed HS_NOALLOC_SCRATCH_BYTES.
+ * Calls no hipMalloc, hipFree or other allocating routine. */
+#define HS_NOALLOC_SCRATCH_BYTES (16 << 20)
+hs_status hs_decode_step_noalloc(const hs_select_params* p, const hs_kv_cache* kv,
+                                 const void* q, const hs_summaries* fine,
+                                 const hs_summaries* coarse, int32_t refresh_begin, float scale,
+                                 int32_t* block_ids, int32_t* num_selected, float* out,
+                                 void* stream);
+
 /* Reads the status word of a workspace of hs_select_decode / hs_decode_step
  * into *status (0, or HS_STEP_WAIT_EXPIRED once a call on the workspace had
  * an expired wait; it stays set until the caller zero-fills the workspace

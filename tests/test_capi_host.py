@@ -242,3 +242,36 @@ def test_select_ratio_and_forced_validation():
     # with a ratio the k of max_blocks blocks counts: int(4096 * 0.05) = 204 -> 221 rows
     assert sel_size(P(ratio=0.05, ms=220), kv, fine)[0] == hs.HS_ERR_INVALID_ARG
     assert sel_size(P(ratio=0.05, ms=221), kv, fine)[0] == hs.HS_OK
+
+
+def test_noalloc_step_refuses_before_any_hip_call():
+    """hs_decode_step_noalloc checks its arguments and the step's workspace
+    size against HS_NOALLOC_SCRATCH_BYTES before any HIP call (this host has
+    no GPU): a step too large for the array is refused with HS_ERR_WORKSPACE,
+    bad arguments with HS_ERR_INVALID_ARG."""
+    L = hs.lib()
+    fine = summ()
+    nb = ctypes.c_size_t(0)
+
+    def call(p, kv, refresh=4095, q=FAKE + (1 << 20)):
+        return L.hs_decode_step_noalloc(ctypes.byref(p), ctypes.byref(kv), q, ctypes.byref(fine),
+                                        None, refresh, ctypes.c_float(0.0), FAKE + (2 << 20),
+                                        FAKE + (3 << 20), FAKE + (4 << 20), None)
+
+    # 256 sequences x 8 KV heads at 128K: 2048 units of 4096 scores (32 MiB)
+    # alone, beyond the 16 MiB array
+    kv = kv_struct(batch=256, num_phys_pages=256 * 4096)
+    p = hs.hs_select_params(32, 128, 512, 0, 145)
+    assert L.hs_select_decode_workspace_size(ctypes.byref(p), ctypes.byref(kv),
+                                             ctypes.byref(fine), None,
+                                             ctypes.byref(nb)) == hs.HS_OK
+    assert nb.value > hs.NOALLOC_SCRATCH_BYTES
+    assert call(p, kv) == hs.HS_ERR_WORKSPACE
+    small = kv_struct()  # the 128K workload itself fits
+    assert L.hs_select_decode_workspace_size(ctypes.byref(p), ctypes.byref(small),
+                                             ctypes.byref(fine), None,
+                                             ctypes.byref(nb)) == hs.HS_OK
+    assert nb.value <= hs.NOALLOC_SCRATCH_BYTES
+    assert call(p, small, refresh=-1) == hs.HS_ERR_INVALID_ARG
+    assert call(p, small, q=FAKE + 2) == hs.HS_ERR_INVALID_ARG
+    assert call(hs.hs_select_params(32, 128, 512, 0, 10), small) == hs.HS_ERR_INVALID_ARG
