@@ -1091,7 +1091,7 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       // more blocks than waves, or long blocks: rebuild, store, and score the
       // stored rows (device-coherent loads)
       for (int beta = r0 + wave; beta < r1; beta += kWaves)
-        summarize_block<TE, D, KIND>(kv, const_cast<void*>(p.summ),
+        summarize_block<TE, D, KIND, 4>(kv, const_cast<void*>(p.summ),
                                      (int64_t)unit * p.max_blocks + beta, b, g, beta,
                                      p.block_size, ug.T);
       __builtin_amdgcn_s_waitcnt(0);  // rebuilt rows are stored

@@ -47,31 +47,39 @@ __device__ __forceinline__ void load_rows(const KvView& kv, const uint8_t* pool,
   }
 }
 
-// Summary row of block beta (tokens [beta S, min(beta S + S, T))) of unit
-// (b, g), by the calling wave, stored at row `row` of `out` (mean: float32
-// [max_blocks][D] per unit; min/max: TE [max_blocks][2][D]).
-template <typename TE, int D, int KIND>
-__device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int64_t row, int b,
-                                                int g, int beta, int S, int T) {
+// Summation order of a block's mean (every path that builds a summary row
+// uses it, so the rows are bitwise equal whichever kernel built them): the
+// block is cut into segments of kSummSeg tokens; inside a segment, lane group
+// tg (of the TPW groups a 16-byte load instruction covers) adds the tokens
+// tg, tg + TPW, ... in increasing order, and the groups are then combined
+// across lanes; the segment sums are added in segment order. Min and max are
+// exact in any order.
+constexpr int kSummSeg = 128;
+
+// Combined values of tokens [t_lo, t_hi) of unit (b, g) for this lane's
+// dims (every lane ends with them): the sum (mean kinds) in acc0, or the
+// min in acc0 and the max in acc1. U: K loads in flight per lane (any U
+// gives the same values).
+template <typename TE, int D, int KIND, int U>
+__device__ __forceinline__ void summ_segment(const KvView& kv, int b, int g, int t_lo, int t_hi,
+                                             float (&acc0)[Vec16<TE>::EPL],
+                                             float (&acc1)[Vec16<TE>::EPL]) {
   constexpr int EPL = Vec16<TE>::EPL;
   constexpr int LPT = D / EPL;      // lanes per token row
   constexpr int TPW = kWave / LPT;  // tokens per wave instruction
   const int lane = thread_id() & (kWave - 1);
   const int tg = lane / LPT, li = lane % LPT;
-  const int t0 = beta * S, t1 = min(t0 + S, T);
-
-  float acc0[EPL], acc1[EPL];  // mean: sum in acc0; minmax: min in acc0, max in acc1
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
     acc0[k] = KIND == HS_SUMMARY_MEAN ? 0.f : INFINITY;
     acc1[k] = -INFINITY;
   }
-  for (int base = t0 + tg; base < t1; base += TPW * kSummUnroll) {
-    uint4 r[kSummUnroll];
-    bool ok[kSummUnroll];
-    load_rows<kSummUnroll>(kv, kv.k_pool, b, g, base, TPW, t1, li * 16, r, ok);
+  for (int base = t_lo + tg; base < t_hi; base += TPW * U) {
+    uint4 r[U];
+    bool ok[U];
+    load_rows<U>(kv, kv.k_pool, b, g, base, TPW, t_hi, li * 16, r, ok);
 #pragma unroll
-    for (int u = 0; u < kSummUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
       float f[EPL];
       Vec16<TE>::unpack(r[u], f);
@@ -101,35 +109,51 @@ __device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int
       }
     }
   }
-  if (tg != 0) return;
-  if (KIND == HS_SUMMARY_MEAN) {
-    const float n = (float)(t1 - t0);
-    float* o = reinterpret_cast<float*>(out) + row * D + li * EPL;
+}
+
+// Folds a later segment's values into the running ones (segment order).
+template <typename TE, int KIND>
+__device__ __forceinline__ void summ_fold(float (&acc0)[Vec16<TE>::EPL],
+                                          float (&acc1)[Vec16<TE>::EPL],
+                                          const float (&s0)[Vec16<TE>::EPL],
+                                          const float (&s1)[Vec16<TE>::EPL]) {
 #pragma unroll
-    for (int k = 0; k < EPL; k += 4)
-      *reinterpret_cast<float4*>(o + k) =
-          make_float4(acc0[k] / n, acc0[k + 1] / n, acc0[k + 2] / n, acc0[k + 3] / n);
-  } else {
-    // min and max of stored values are stored values: write them back exactly
-    uint4 lo, hi;
-    if constexpr (EPL == 4) {
-      lo = make_uint4(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]),
-                      __float_as_uint(acc0[2]), __float_as_uint(acc0[3]));
-      hi = make_uint4(__float_as_uint(acc1[0]), __float_as_uint(acc1[1]),
-                      __float_as_uint(acc1[2]), __float_as_uint(acc1[3]));
+  for (int k = 0; k < Vec16<TE>::EPL; ++k) {
+    if (KIND == HS_SUMMARY_MEAN) {
+      acc0[k] += s0[k];
     } else {
-      auto pack = [](float a, float c) {
-        return (__float_as_uint(a) >> 16) | (__float_as_uint(c) & 0xFFFF0000u);
-      };
-      lo = make_uint4(pack(acc0[0], acc0[1]), pack(acc0[2], acc0[3]), pack(acc0[4], acc0[5]),
-                      pack(acc0[6], acc0[7]));
-      hi = make_uint4(pack(acc1[0], acc1[1]), pack(acc1[2], acc1[3]), pack(acc1[4], acc1[5]),
-                      pack(acc1[6], acc1[7]));
+      acc0[k] = fminf(acc0[k], s0[k]);
+      acc1[k] = fmaxf(acc1[k], s1[k]);
     }
-    uint8_t* o = reinterpret_cast<uint8_t*>(out) + row * 2 * D * (int64_t)sizeof(TE);
-    *reinterpret_cast<uint4*>(o + li * 16) = lo;
-    *reinterpret_cast<uint4*>(o + D * sizeof(TE) + li * 16) = hi;
   }
+}
+
+template <typename TE, int D, int KIND>
+__device__ __forceinline__ void summ_store(void* out, int64_t row,
+                                           const float (&acc0)[Vec16<TE>::EPL],
+                                           const float (&acc1)[Vec16<TE>::EPL], int n_tok);
+
+// Summary row of block beta (tokens [beta S, min(beta S + S, T))) of unit
+// (b, g), by the calling wave alone, segment after segment, stored at row
+// `row` of `out` (mean: float32 [max_blocks][D] per unit; min/max: TE
+// [max_blocks][2][D]).
+template <typename TE, int D, int KIND, int U = kSummUnroll>
+__device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int64_t row, int b,
+                                                int g, int beta, int S, int T) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  const int t0 = beta * S, t1 = min(t0 + S, T);
+  float acc0[EPL], acc1[EPL];
+  if (KIND != HS_SUMMARY_MEAN) {  // min and max: one pass, any order
+    summ_segment<TE, D, KIND, U>(kv, b, g, t0, t1, acc0, acc1);
+  } else {
+    summ_segment<TE, D, KIND, U>(kv, b, g, t0, min(t0 + kSummSeg, t1), acc0, acc1);
+    for (int lo = t0 + kSummSeg; lo < t1; lo += kSummSeg) {
+      float s0[EPL], s1[EPL];
+      summ_segment<TE, D, KIND, U>(kv, b, g, lo, min(lo + kSummSeg, t1), s0, s1);
+      summ_fold<TE, KIND>(acc0, acc1, s0, s1);
+    }
+  }
+  summ_store<TE, D, KIND>(out, row, acc0, acc1, t1 - t0);
 }
 
 // The same summary as summarize_block for a block of at most NL * TPW

@@ -1,5 +1,6 @@
 // summaries.hip - stage 1 as one launch: per-block key summaries from the
-// paged K cache, one wave per block (grid: block groups x units). The device
+// paged K cache (grid: block groups x units), one wave per block, or one
+// workgroup per block for blocks longer than a summation segment. The device
 // code and its sources are in summ_impl.h; the representation phase builds
 // every block, a decode step refreshes only the last, growing block.
 #include "summ_impl.h"
@@ -8,7 +9,10 @@ namespace hs {
 namespace {
 
 constexpr int kWavesPerWG = 4;
+constexpr int kBuildUnroll = 16;  // K loads in flight per lane (the values do not depend on it)
 
+// Blocks of at most kSummSeg tokens: one wave per block, kWavesPerWG blocks
+// per workgroup.
 template <typename TE, int D, int KIND>
 __global__ __launch_bounds__(256) void k_build_summaries(SummParams p) {
   const KvView& kv = p.kv;
@@ -20,15 +24,83 @@ __global__ __launch_bounds__(256) void k_build_summaries(SummParams p) {
   const int T = clamp_len(kv, b);
   const int nb = (T + S - 1) / S;
   if (beta >= nb || beta >= p.max_blocks) return;
-  summarize_block<TE, D, KIND>(kv, p.out, (int64_t)unit * p.max_blocks + beta, b, g, beta, S, T);
+  summarize_block<TE, D, KIND, kBuildUnroll>(kv, p.out, (int64_t)unit * p.max_blocks + beta, b,
+                                             g, beta, S, T);
+}
+
+// Longer blocks: one workgroup per block. In each round its waves reduce the
+// next kWavesPerWG segments side by side and wave 0 folds them, in segment
+// order, into the running values, so the row equals summarize_block's.
+template <typename TE, int D, int KIND>
+__global__ __launch_bounds__(256) void k_build_long_summaries(SummParams p) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int LPT = D / EPL;
+  __shared__ float seg[kWavesPerWG][2][LPT][EPL];  // per wave: [sum or min, max][lane][dim]
+  const KvView& kv = p.kv;
+  const int unit = blockIdx.y;
+  const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int S = p.block_size;
+  const int beta = p.block_begin + blockIdx.x;
+  const int T = clamp_len(kv, b);
+  const int nb = (T + S - 1) / S;
+  if (beta >= nb || beta >= p.max_blocks) return;  // uniform over the workgroup
+  const int t0 = beta * S, t1 = min(t0 + S, T);
+  const int nseg = (t1 - t0 + kSummSeg - 1) / kSummSeg;
+  float acc0[EPL], acc1[EPL];
+  for (int r = 0; r < nseg; r += kWavesPerWG) {
+    const int sg = r + wave;
+    if (sg < nseg) {
+      float s0[EPL], s1[EPL];
+      const int lo = t0 + sg * kSummSeg;
+      summ_segment<TE, D, KIND, kBuildUnroll>(kv, b, g, lo, min(lo + kSummSeg, t1), s0, s1);
+      if (lane < LPT) {  // token group 0 holds the segment's values
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          seg[wave][0][lane][k] = s0[k];
+          seg[wave][1][lane][k] = s1[k];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int li = lane % LPT;
+      for (int w = 0; w < kWavesPerWG && r + w < nseg; ++w) {
+        float s0[EPL], s1[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          s0[k] = seg[w][0][li][k];
+          s1[k] = seg[w][1][li][k];
+        }
+        if (r + w == 0) {
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) {
+            acc0[k] = s0[k];
+            acc1[k] = s1[k];
+          }
+        } else {
+          summ_fold<TE, KIND>(acc0, acc1, s0, s1);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0)
+    summ_store<TE, D, KIND>(p.out, (int64_t)unit * p.max_blocks + beta, acc0, acc1, t1 - t0);
 }
 
 template <typename TE, int D>
-hipError_t launch_td(const SummParams& p, dim3 grid, hipStream_t s) {
-  if (p.kind == HS_SUMMARY_MEAN)
+hipError_t launch_td(const SummParams& p, dim3 grid, bool longb, hipStream_t s) {
+  if (longb) {
+    if (p.kind == HS_SUMMARY_MEAN)
+      hipLaunchKernelGGL((k_build_long_summaries<TE, D, HS_SUMMARY_MEAN>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_build_long_summaries<TE, D, HS_SUMMARY_MINMAX>), grid, dim3(256), 0, s, p);
+  } else if (p.kind == HS_SUMMARY_MEAN) {
     hipLaunchKernelGGL((k_build_summaries<TE, D, HS_SUMMARY_MEAN>), grid, dim3(256), 0, s, p);
-  else
+  } else {
     hipLaunchKernelGGL((k_build_summaries<TE, D, HS_SUMMARY_MINMAX>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -39,11 +111,12 @@ hipError_t launch_build_summaries(const SummParams& p, hipStream_t s) {
   const int nb_max = (p.kv.max_seq_len + S - 1) / S;
   const int n = (nb_max < p.max_blocks ? nb_max : p.max_blocks) - p.block_begin;
   if (n <= 0) return hipSuccess;
-  dim3 grid((n + kWavesPerWG - 1) / kWavesPerWG, p.kv.batch * p.kv.num_kv_heads);
+  const bool longb = S > kSummSeg;
+  dim3 grid(longb ? n : (n + kWavesPerWG - 1) / kWavesPerWG, p.kv.batch * p.kv.num_kv_heads);
   const bool bf = p.kv.elem_bytes == 2;
   if (p.kv.head_dim == 64)
-    return bf ? launch_td<bf16_t, 64>(p, grid, s) : launch_td<float, 64>(p, grid, s);
-  return bf ? launch_td<bf16_t, 128>(p, grid, s) : launch_td<float, 128>(p, grid, s);
+    return bf ? launch_td<bf16_t, 64>(p, grid, longb, s) : launch_td<float, 64>(p, grid, longb, s);
+  return bf ? launch_td<bf16_t, 128>(p, grid, longb, s) : launch_td<float, 128>(p, grid, longb, s);
 }
 
 }  // namespace hs
