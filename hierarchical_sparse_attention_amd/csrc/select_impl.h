@@ -46,6 +46,7 @@ constexpr int kBinsPerThread = kBins / kThreads;
 constexpr int kRegKeys = 16;    // keys per thread of the register path (<= 4096 candidates)
 constexpr int kLdsKeys = 8192;  // beyond this many candidates keys stay in the workspace
 constexpr int kMaxCand = 128;   // a threshold bin this small is ranked directly
+static_assert(kMaxCand % 8 == 0, "bin ranking reads candidates in groups of 8");
 
 // Number of scoring tasks of a unit for a level with n_slots_max candidates.
 __host__ __device__ inline int select_chunks(int n_slots_max) {
@@ -60,11 +61,19 @@ struct SlotMap {
     if (gamma == nullptr) return c < nb ? c : -1;
     const int gi = c / ratio;
     if (gi >= gcnt) return -1;
-    const int g = gamma[gi];
-    const int beta = g * ratio + c % ratio;
+    return from_entry(gamma[gi], c - gi * ratio);
+  }
+  // block of the slot at offset r of coarse entry g (-1 if none)
+  __device__ __forceinline__ int from_entry(int g, int r) const {
+    const int beta = g * ratio + r;
     return g >= 0 && beta < nb ? beta : -1;
   }
 };
+
+// Coarse entries of one scoring chunk staged in LDS, so that a row's block
+// costs an LDS read instead of a dependent global load (a chunk of
+// kRowsPerWG slots spans at most kRowsPerWG entries).
+constexpr int kGammaLds = 512;
 
 // What a unit looks like to one selection level: T (clamped), its number of
 // blocks nb, its candidate slots and their count n.
@@ -115,6 +124,7 @@ struct TopkShared {
   __attribute__((aligned(16))) float xpose[kThreads * kRegKeys];  // scores, transposed
   uint32_t cand_key[kWaves][kMaxCand];   // threshold-bin keys (up to kMaxCand + 7 read)
   int32_t cand_slot[kWaves][kMaxCand];
+  int32_t cand_blk[kWaves][kMaxCand];    // their blocks (register path)
   uint32_t tie_cnt[kRegKeys][kWaves];
   __attribute__((aligned(16))) uint32_t scan_tot[3][kWaves];  // wave totals of three scans
   float stage[kRowsPerWG];                     // scores of this workgroup's rows
@@ -125,6 +135,7 @@ struct TopkShared {
   uint32_t kbits[kThreads * kRegKeys / 32];  // threshold-bin candidates ranked into the top-k
   uint32_t n_cand;                           // threshold-bin candidates gathered
   int last;
+  int32_t gam[kGammaLds];                    // staged coarse entries (see kGammaLds)
 };
 
 // ----------------------------------------------------- wave-level scans (DPP)
@@ -532,20 +543,47 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
     __syncthreads();
     return;
   }
-  auto block_of = [&](int c) { return TWO ? ug.slots.block_of(c) : c; };
   const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
   float v[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u)  // unconditional (clamped), coalesced loads that overlap
     v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
+  // the block of each of this thread's candidates (-1: none). TWO: slot c is
+  // offset c % ratio of coarse entry c / ratio; quotient and remainder are
+  // stepped from candidate to candidate (no division each), and the entries
+  // are loaded with the scores (gcnt >= 1 here, since n > 0).
+  int blk[KPT];
+  if (TWO) {
+    const int ratio = ug.slots.ratio, gc = ug.slots.gcnt;
+    const int dq = kThreads / ratio, dr = kThreads - dq * ratio;
+    int gi = tid / ratio, r = tid - gi * ratio;
+    int ent[KPT], gis[KPT], off[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      gis[u] = gi;
+      off[u] = r;
+      ent[u] = ug.slots.gamma[min(gi, gc - 1)];
+      gi += dq;
+      r += dr;
+      if (r >= ratio) {
+        r -= ratio;
+        ++gi;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      blk[u] = u * kThreads + tid < n && gis[u] < gc ? ug.slots.from_entry(ent[u], off[u]) : -1;
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) blk[u] = u * kThreads + tid < n ? u * kThreads + tid : -1;
+  }
   // the first histogram is cleared while the loads are in flight
   for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
   uint32_t kr[KPT];
   uint32_t cnt = 0, kmax = 0, kmin_inv = 0;  // kmin_inv: largest ~key
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int c = u * kThreads + tid;
-    const bool ok = c < n && (!TWO || ug.slots.block_of(c) >= 0);
+    const bool ok = blk[u] >= 0;
     const uint32_t k = ok ? order_key(v[u]) : 0u;
     kr[u] = k;
     kmax = max(kmax, k);
@@ -576,7 +614,7 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
   if (k_eff == n_valid) {  // every candidate is kept
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
-      if (kr[u]) mark(bitmap, block_of(u * kThreads + tid));
+      if (kr[u]) mark(bitmap, blk[u]);
     return;
   }
   // Threshold: after the loop every key > pmax is kept, every key < prefix is
@@ -618,15 +656,15 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
     const uint32_t k = kr[u];
-    const int c = u * kThreads + tid;
     const bool inb = k != 0 && k >= prefix && k <= pmax;
-    if (k > pmax || (take_bin && inb)) mark(bitmap, block_of(c));
+    if (k > pmax || (take_bin && inb)) mark(bitmap, blk[u]);
     if (rank_bin) {
       const uint64_t m = __ballot(inb);
       if (inb) {
         const uint32_t pos = wrun + (uint32_t)__popcll(m & below);
         sh.cand_key[wave][pos] = k;
-        sh.cand_slot[wave][pos] = c;
+        sh.cand_slot[wave][pos] = u * kThreads + tid;
+        sh.cand_blk[wave][pos] = blk[u];
       }
       wrun += (uint32_t)__popcll(m);
     }
@@ -645,16 +683,23 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
     }
     if (w >= 0) {
       const uint32_t kt = sh.cand_key[w][tid - first];
-      const int ct = sh.cand_slot[w][tid - first];
+      const int ct = sh.cand_slot[w][tid - first], bt = sh.cand_blk[w][tid - first];
       uint32_t rank = 0;
 #pragma unroll
       for (int w2 = 0; w2 < kWaves; ++w2)
-        for (uint32_t j = 0; j < wc[w2]; ++j) {
-          const uint32_t kj = sh.cand_key[w2][j];
-          const int cj = sh.cand_slot[w2][j];
-          rank += (kj > kt || (kj == kt && cj < ct)) ? 1u : 0u;
+        for (uint32_t j0 = 0; j0 < wc[w2]; j0 += 8) {  // 8 loads per LDS round trip
+          uint32_t k2[8];
+          int c2[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {  // j0 + i < kMaxCand (a multiple of 8); later ones ignored
+            k2[i] = sh.cand_key[w2][j0 + i];
+            c2[i] = sh.cand_slot[w2][j0 + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            rank += (j0 + i < wc[w2] && (k2[i] > kt || (k2[i] == kt && c2[i] < ct))) ? 1u : 0u;
         }
-      if (rank < remaining) mark(bitmap, block_of(ct));
+      if (rank < remaining) mark(bitmap, bt);
     }
   } else if (!take_bin) {
     // more than kMaxCand keys all equal to the threshold: the first
@@ -680,7 +725,7 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
       }
       if (kr[u] != 0 && kr[u] == prefix &&
           before + waves_before + (uint32_t)__popcll(tie_mask[u] & below) < remaining)
-        mark(bitmap, block_of(u * kThreads + tid));
+        mark(bitmap, blk[u]);
       before += in_slot;
     }
   }
@@ -980,10 +1025,22 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   const int c_begin = c_wg + wave * kRowsPerWave;
   const int li = lane % LPR, rg = lane / LPR;
   static_assert(kRowsPerWG <= kThreads, "at most one staged score per thread");
+  static_assert(kRowsPerWG <= kGammaLds, "a chunk's coarse entries fit the staging array");
   if constexpr (kTok) {  // a staged row that holds no token keeps the absent score
     if (tid < kRowsPerWG) sh.stage[tid] = __uint_as_float(kAbsentScore);
-    __syncthreads();
   }
+  // Slots map to blocks through coarse entries (two levels, token level):
+  // the chunk's entries [g_lo, g_hi) are staged in LDS first (their loads
+  // overlap the query loads below), so that no row load waits on a lookup.
+  const bool via_gamma = ug.slots.gamma != nullptr;  // uniform
+  const int g_lo = via_gamma ? c_wg / p.ratio : 0;
+  const int g_hi = via_gamma ? min((c_wg + kRowsPerWG - 1) / p.ratio + 1, ug.slots.gcnt) : 0;
+  for (int i = tid; i < g_hi - g_lo; i += kThreads) sh.gam[i] = ug.slots.gamma[g_lo + i];
+  auto block_of = [&](int c) {
+    if (!via_gamma) return ug.slots.block_of(c);
+    const int gi = c / p.ratio;
+    return gi < g_hi ? ug.slots.from_entry(sh.gam[gi - g_lo], c - gi * p.ratio) : -1;
+  };
 
   // the unit's G query heads folded into per-element coefficients
   float coef[EPS];
@@ -1004,6 +1061,7 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       coef[k] = c;
     }
   }
+  if (via_gamma || kTok) __syncthreads();  // staged coarse entries, absent scores of token rows
   // score of one row from the EPS elements each of its LPR lanes holds
   auto row_dot = [&](const float (&f)[EPS]) {
     float acc = 0.f;
@@ -1053,14 +1111,14 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
                       (int64_t)kv.head_dim * kv.elem_bytes;
             }
           } else {
-            const int beta = c < c_end ? ug.slots.block_of(c) : -1;
+            const int beta = c < c_end ? block_of(c) : -1;
             off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
           }
           cs[u] = off >= 0 ? c : -1;
           r[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
                           : make_uint4(0, 0, 0, 0);
         } else {
-          const int beta = c < c_end ? ug.slots.block_of(c) : -1;
+          const int beta = c < c_end ? block_of(c) : -1;
           cs[u] = beta >= 0 ? c : -1;
           r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
                            : make_uint4(0, 0, 0, 0);
@@ -1113,7 +1171,7 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   const bool in = tid < kRowsPerWG && c < n_slots;
   bool ok;
   if constexpr (kTok) ok = in && __float_as_uint(sh.stage[tid]) != kAbsentScore;
-  else ok = in && ug.slots.block_of(c) >= 0;
+  else ok = in && block_of(c) >= 0;
   uint32_t kx = 0, ki = 0;
   if (ok) {
     const float v = sh.stage[tid];
