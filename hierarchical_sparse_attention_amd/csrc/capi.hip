@@ -290,8 +290,7 @@ hs::DecodeParams decode_params(const hs_kv_cache* kv, const void* q, float scale
 // and the level's parameters.
 struct TokenLayout {
   int64_t units, n_slots;
-  int32_t ppb;  // pages per block when the block size is a multiple of the page size, else 0
-  size_t off_cnt, off_scores, off_keys, off_pages, total;
+  size_t off_cnt, off_scores, off_keys, total;
 };
 
 hs_status check_tokens(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block_size,
@@ -309,17 +308,17 @@ hs_status check_tokens(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
   const int64_t need = std::min<int64_t>(n_slots, top_k_tokens) +
                        std::min<int64_t>(window_tokens, kv->max_seq_len);
   if (max_tokens < need) return HS_ERR_INVALID_ARG;
-  if (hs::select_launch_lds_bytes(kv->max_seq_len, (int32_t)n_slots, max_tokens) > (64u << 10))
+  if (!hs::tokens_in_registers(hs::kKindTokens, (int32_t)n_slots, max_selected) &&
+      hs::select_launch_lds_bytes(kv->max_seq_len, (int32_t)n_slots, max_tokens) >
+          (size_t)HS_TOKEN_LDS_BYTES)
     return HS_ERR_UNSUPPORTED;
   L->units = (int64_t)kv->batch * kv->num_kv_heads;
   L->n_slots = n_slots;
   L->off_cnt = 0;
   L->off_scores = align_up(sizeof(int32_t) * hs::kCounterStride * L->units);
   L->off_keys = align_up(L->off_scores + sizeof(float) * L->units * n_slots);
-  L->off_pages = align_up(L->off_keys + sizeof(uint32_t) * 2 * L->units *
-                                            hs::step_chunks((int32_t)n_slots));
-  L->ppb = block_size % kv->page_size == 0 ? block_size / kv->page_size : 0;
-  L->total = align_up(L->off_pages + sizeof(int32_t) * 2 * L->units * max_selected * L->ppb);
+  L->total = align_up(L->off_keys + sizeof(uint32_t) * 2 * L->units *
+                                         hs::step_chunks((int32_t)n_slots));
   return HS_OK;
 }
 
@@ -379,14 +378,7 @@ hs_status hs_select_tokens(const hs_kv_cache* kv, const void* q, int32_t num_q_h
   sp.out_blocks_max = kv->max_seq_len;
   sp.counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
   sp.refresh_begin = -1;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (L.ppb > 0) {  // resolve the selected blocks' pages once per unit
-    sp.tok_pages = reinterpret_cast<int2*>(ws + L.off_pages);
-    sp.tok_ppb = L.ppb;
-    const hipError_t e = hs::launch_tok_pages(sp, s);
-    if (e != hipSuccess) return from_hip(e);
-  }
-  return from_hip(hs::launch_select(sp, s));
+  return from_hip(hs::launch_select(sp, static_cast<hipStream_t>(stream)));
 }
 
 

@@ -240,19 +240,15 @@ struct SelectParams {
   int32_t out_blocks_max;    // blocks of this level per unit (bitmap bits)
   int32_t* counters;         // [units] workgroup arrivals; zero between calls
   int32_t refresh_begin;     // >= 0: rebuild blocks from here on before scoring (single level)
-  // token level with block size a multiple of the page size: per selected block
-  // (gamma entry) its tok_ppb pages as (physical page, tokens of it below T_b),
-  // [units][gamma_cap][tok_ppb], filled by launch_tok_pages; else null
-  int2* tok_pages = nullptr;
-  int32_t tok_ppb = 0;
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
-// Fills p.tok_pages (one workgroup per unit) from the block ids and the page table.
-hipError_t launch_tok_pages(const SelectParams& p, hipStream_t s);
 // Dynamic LDS of a selection workgroup: bitmap words, then keys (general path).
 size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max);
 // Total dynamic LDS of a k_select launch (adds the staged id list).
 size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap);
+// Whether a selection of this kind and size takes the token level's register
+// path, which needs no dynamic LDS (no bitmap, no staged list).
+bool tokens_in_registers(int32_t kind, int32_t n_slots_max, int32_t gamma_cap);
 
 struct DecodeParams {
   KvView kv;

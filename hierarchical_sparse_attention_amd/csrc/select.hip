@@ -7,49 +7,40 @@ namespace hs {
 namespace {
 
 // dynamic LDS: [bitmap][keys of the general path][id list, out_cap + kWave]
+// The token level asks for 3 waves per SIMD (at most 168 VGPRs), so that its
+// (chunks x units) workgroups are resident together at the bench shapes.
 template <typename TE, int D, int KIND, int G>
-__global__ __launch_bounds__(kThreads) void k_select(SelectParams p, int list_off) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(KIND == kKindTokens ? 3 : 1))) void k_select(
+    SelectParams p, int list_off) {
   __shared__ TopkShared sh;
   extern __shared__ uint32_t dyn[];
   select_task<TE, D, KIND, G>(p, blockIdx.y, blockIdx.x, gridDim.x, sh, dyn,
                               reinterpret_cast<int32_t*>(dyn + list_off));
 }
 
-// One workgroup per unit: the pages of each selected block, in order, with the
-// number of each page's tokens below the unit's length (0: no token, e.g. an
-// absent entry, a page past T_b or an invalid page id).
-__global__ __launch_bounds__(kThreads) void k_tok_pages(SelectParams p) {
-  const int unit = blockIdx.x, b = unit / p.kv.num_kv_heads;
-  const UnitGeom ug = unit_geom(p, unit);
-  const int S = p.ratio, P = p.kv.page_size, ppb = p.tok_ppb;
-  int2* out = p.tok_pages + (int64_t)unit * p.gamma_cap * ppb;
-  for (int i = threadIdx.x; i < p.gamma_cap * ppb; i += kThreads) {
-    const int gi = i / ppb, j = i - gi * ppb;
-    int page = 0, lim = 0;
-    const int gg = gi < ug.slots.gcnt ? ug.slots.gamma[gi] : -1;
-    if (gg >= 0) {
-      const int64_t t0 = (int64_t)gg * S + (int64_t)j * P;  // first token of the page
-      if (t0 < ug.nb) {
-        const int pg = p.kv.page_table[(int64_t)b * p.kv.max_pages + (int)(t0 / P)];
-        if ((unsigned)pg < (unsigned)p.kv.num_phys_pages) {
-          page = pg;
-          lim = (int)min((int64_t)P, (int64_t)ug.nb - t0);
-        }
-      }
-    }
-    out[i] = make_int2(page, lim);
+static_assert(sizeof(TopkShared) + HS_TOKEN_LDS_BYTES <= (160u << 10),
+              "a token-level workgroup fits the LDS of a gfx950 workgroup");
+
+template <typename TE, int D, int KIND, int G>
+hipError_t launch_one(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
+  const void* k = reinterpret_cast<const void*>(&k_select<TE, D, KIND, G>);
+  if (lds > (64u << 10)) {  // above the default limit of dynamic LDS
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL((k_select<TE, D, KIND, G>), grid, dim3(kThreads), lds, s, p, list_off);
+  return hipGetLastError();
 }
 
 template <typename TE, int D, int KIND>
 hipError_t launch_g(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((k_select<TE, D, KIND, 1>), grid, dim3(kThreads), lds, s, p, list_off); break;
-    case 2: hipLaunchKernelGGL((k_select<TE, D, KIND, 2>), grid, dim3(kThreads), lds, s, p, list_off); break;
-    case 4: hipLaunchKernelGGL((k_select<TE, D, KIND, 4>), grid, dim3(kThreads), lds, s, p, list_off); break;
-    default: hipLaunchKernelGGL((k_select<TE, D, KIND, 8>), grid, dim3(kThreads), lds, s, p, list_off); break;
+    case 1: return launch_one<TE, D, KIND, 1>(p, grid, lds, list_off, s);
+    case 2: return launch_one<TE, D, KIND, 2>(p, grid, lds, list_off, s);
+    case 4: return launch_one<TE, D, KIND, 4>(p, grid, lds, list_off, s);
+    default: return launch_one<TE, D, KIND, 8>(p, grid, lds, list_off, s);
   }
-  return hipGetLastError();
 }
 
 template <typename TE, int D>
@@ -68,20 +59,22 @@ size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max) {
   return sizeof(uint32_t) * (words + keys);
 }
 
-size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap) {
-  return select_lds_bytes(out_blocks_max, n_slots_max) + sizeof(uint32_t) * ((size_t)out_cap + kWave);
+bool tokens_in_registers(int32_t kind, int32_t n_slots_max, int32_t gamma_cap) {
+  return kind == kKindTokens && n_slots_max <= kThreads * kTokKeys && gamma_cap <= kGammaLds;
 }
 
-hipError_t launch_tok_pages(const SelectParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_tok_pages, dim3(p.kv.batch * p.kv.num_kv_heads), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap) {
+  return select_lds_bytes(out_blocks_max, n_slots_max) + sizeof(uint32_t) * ((size_t)out_cap + kWave);
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   const dim3 grid(select_chunks(p.n_slots_max),
                   p.kv.batch * p.kv.num_kv_heads);
   const int list_off = (int)(select_lds_bytes(p.out_blocks_max, p.n_slots_max) / sizeof(uint32_t));
-  const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.out_cap + kWave);
+  // the token level's register path (topk_tokens) uses static LDS only
+  const size_t lds = tokens_in_registers(p.kind, p.n_slots_max, p.gamma_cap)
+                         ? 0
+                         : sizeof(uint32_t) * ((size_t)list_off + p.out_cap + kWave);
   const bool bf = p.kv.elem_bytes == 2;
   if (p.kv.head_dim == 64)
     return bf ? launch_k<bf16_t, 64>(p, grid, lds, list_off, s)

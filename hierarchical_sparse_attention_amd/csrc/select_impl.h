@@ -329,16 +329,18 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
   float v[KPT];
   uint32_t kmax = 0, kmin_inv = 0;
-  if (n > 0) {
+  {
     // coalesced loads (thread t: candidates u * 256 + t), transposed through
-    // LDS to the contiguous ownership; thread t < nch loads chunk t's key
-    // range in the same round trip
+    // LDS to the contiguous ownership; every chunk's key range in the same
+    // round trip. Bounded by the capacity, not by n, so that they do not
+    // wait for the load of the unit's length (chunks past n published empty
+    // ranges; candidates past n are masked below).
+    const int nmax = p.n_slots_max;
 #pragma unroll
     for (int u = 0; u < KPT; ++u)  // unconditional (clamped) loads that overlap
-      v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
-    const int nch = (n + kRowsPerWG - 1) / kRowsPerWG;
-    const int32_t* ck = reinterpret_cast<const int32_t*>(
-        p.chunk_keys + (int64_t)unit * select_chunks(p.n_slots_max) * 2);
+      v[u] = published(&sc[min(u * kThreads + tid, nmax - 1)]);
+    const int nch = select_chunks(nmax);
+    const int32_t* ck = reinterpret_cast<const int32_t*>(p.chunk_keys + (int64_t)unit * nch * 2);
     for (int ch = tid; ch < nch; ch += kThreads) {
       kmax = max(kmax, (uint32_t)published_i32(&ck[2 * ch]));
       kmin_inv = max(kmin_inv, (uint32_t)published_i32(&ck[2 * ch + 1]));
@@ -367,7 +369,7 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
     const int f = forced[i];
     if (f >= 0 && f < n) atomicOr(&sh.kbits[f >> 5], 1u << (f & 31));
   }
-  if (n > 0) {
+  {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       kmax = max(kmax, sh.red[1][w]);
@@ -526,6 +528,288 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   return cnt;
 }
 
+// Token level with at most kThreads * kTokKeys candidate slots and at most
+// kGammaLds selected blocks ("SparDA" article, section 2.3: a finer pass
+// keeps single tokens inside the chosen blocks). Slot c is token gamma[c / S] * S + c % S of the unit's block list
+// (S = p.ratio); the list is ascending, so slot order is token order. Kept:
+// the first min(k, #candidates) candidates by (score desc, slot asc), plus
+// every token of the window [T - W, T), candidate or not. Thread t owns
+// slots 32t .. 32t + 31, so its keep decisions are the bits of one word and
+// the ascending output is one workgroup scan: the kept candidates below the
+// window in slot order, then the window's tokens. No bitmap over the
+// sequence is needed. Writes the ids and the count to gids / gcnt.
+constexpr int kTokKeys = 32;
+// The float whose order_key is k (+0 for the key of -0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+static_assert(kThreads * kTokKeys / 32 <= kThreads * kRegKeys,
+              "ranked-kept bits fit the transposition array");
+static_assert(kTokKeys == 32, "one word of keep bits per thread");
+
+__device__ __forceinline__ void topk_tokens(const SelectParams& p, int unit, const UnitGeom& ug,
+                                            TopkShared& sh, int32_t* gids, int32_t* gcnt) {
+  constexpr int KPT = kTokKeys;
+  constexpr int HALF = kThreads * KPT / 2;  // slots transposed per round
+  const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
+  const int n = ug.n, S = p.ratio, T = ug.T;
+  const int c0 = KPT * tid;  // first slot of this thread
+  const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
+  float v[KPT];
+  uint32_t kmax = 0, kmin_inv = 0;
+  {
+    // One round trip: coalesced score loads (thread t: slots u * 256 + t),
+    // every chunk's key range and the block list, all bounded by the
+    // capacities rather than the unit's counts (applied below), so that
+    // none of them waits for the count's load. Chunks past the unit's slots
+    // published empty ranges; slots past them are masked below.
+    const int nmax = p.n_slots_max;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) v[u] = published(&sc[min(u * kThreads + tid, nmax - 1)]);
+    const int nch = select_chunks(nmax);
+    const int32_t* ck = reinterpret_cast<const int32_t*>(p.chunk_keys + (int64_t)unit * nch * 2);
+    for (int ch = tid; ch < nch; ch += kThreads) {
+      kmax = max(kmax, (uint32_t)published_i32(&ck[2 * ch]));
+      kmin_inv = max(kmin_inv, (uint32_t)published_i32(&ck[2 * ch + 1]));
+    }
+    // the block list, staged in LDS for the token ids of the emission
+    for (int i = tid; i < p.gamma_cap; i += kThreads) sh.gam[i] = ug.slots.gamma[i];
+    kmax = wave_max_u(kmax);
+    kmin_inv = wave_max_u(kmin_inv);
+    if (lane == 0) {
+      sh.red[1][wave] = kmax;
+      sh.red[2][wave] = kmin_inv;
+    }
+  }
+  for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+  if (tid == 0) sh.n_cand = 0u;
+  // transposition to the contiguous ownership, HALF slots per round: the
+  // threads of half h own slots [h * HALF, (h + 1) * HALF)
+  // (keys: 0 = no candidate)
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h) __syncthreads();  // the first round has been read
+#pragma unroll
+    for (int u = 0; u < KPT / 2; ++u) sh.xpose[u * kThreads + tid] = v[h * KPT / 2 + u];
+    __syncthreads();
+    if (tid / (kThreads / 2) == h) {
+#pragma unroll
+      for (int u = 0; u < KPT; u += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&sh.xpose[c0 - h * HALF + u]);
+        kr[u] = order_key(x.x);
+        kr[u + 1] = order_key(x.y);
+        kr[u + 2] = order_key(x.z);
+        kr[u + 3] = order_key(x.w);
+      }
+    }
+  }
+  uint32_t present = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    kr[u] = c0 + u < n ? kr[u] : 0u;
+    present |= (kr[u] != 0 ? 1u : 0u) << u;
+  }
+  const uint32_t cnt = wave_sum_u((uint32_t)__popc(present));
+  if (lane == 0) sh.red[0][wave] = cnt;
+  __syncthreads();  // key counts and ranges; the transposition array is free
+  uint32_t* rbits = reinterpret_cast<uint32_t*>(sh.xpose);  // ranked-kept bits, word t: thread t
+  rbits[tid] = 0u;
+  uint32_t n_valid = 0;
+  kmax = 0;
+  kmin_inv = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    n_valid += sh.red[0][w2];
+    kmax = max(kmax, sh.red[1][w2]);
+    kmin_inv = max(kmin_inv, sh.red[2][w2]);
+  }
+  const uint32_t kmin = ~kmin_inv;
+  const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
+  // Threshold by buckets over the candidates' own range. The first pass
+  // buckets linearly in value over [vmin, vmax] (rounded float arithmetic is
+  // monotone, and the keys spread over all the buckets, so the histogram's
+  // atomics rarely collide; a radix digit of the leading key bits would put
+  // them in a few exponent buckets). While the threshold's bucket holds more
+  // than kMaxCand candidates, the next pass buckets that bucket's own
+  // [min, max] in key order (fixed-width buckets from its min), which always
+  // splits it. Candidates above
+  // the threshold's bucket are kept; its own are ranked, or taken whole.
+  const bool keep_all = k_eff > 0 && k_eff == n_valid;
+  uint32_t keep = keep_all ? present : 0u;
+  uint32_t cand = 0, remaining = 0, in_bin = 0;  // cand: the threshold bucket's candidates
+  int mode = 0;                                  // 1: all equal, 2: rank (uniform)
+  if (k_eff > 0 && !keep_all) {                  // uniform
+    remaining = k_eff;
+    cand = present;
+    in_bin = n_valid;
+    uint32_t lo = kmin, hi = kmax;
+    const float vlo = key_value(lo), width = key_value(hi) - vlo;
+    const float vscale = (float)kBins / width;
+    bool by_value = width > 0.f && __builtin_isfinite(width) && __builtin_isfinite(vscale);
+    for (;;) {
+      if (lo == hi) {
+        mode = 1;
+        break;
+      }
+      // this pass's bucket of every candidate (the dummy bin of the lane for
+      // the others); key buckets are (k - lo) >> sh_k with (hi - lo) >> sh_k
+      // in [kBins / 2, kBins)
+      const int sh_k = max(0, 32 - __clz(hi - lo) - kDigitBits);
+      uint32_t bk[KPT];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const uint32_t b = by_value
+            ? min((uint32_t)((key_value(kr[u]) - vlo) * vscale), (uint32_t)(kBins - 1))
+            : (kr[u] - lo) >> sh_k;
+        bk[u] = (cand >> u) & 1u ? b : (uint32_t)(kBins + lane);
+        atomicAdd(&sh.hist[bk[u]], 1u);
+      }
+      __syncthreads();
+      uint32_t d = 0;
+      in_bin = take_digit_flat(sh, kBins, 0, d, remaining);
+      uint32_t next = 0;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {  // dummy bins are above every bucket but not candidates
+        const bool c = (cand >> u) & 1u;
+        keep |= (c && bk[u] > d ? 1u : 0u) << u;
+        next |= (c && bk[u] == d ? 1u : 0u) << u;
+      }
+      cand = next;
+      if (in_bin == remaining) {  // the whole bucket is kept
+        keep |= cand;
+        break;
+      }
+      if (in_bin <= (uint32_t)kMaxCand) {
+        mode = 2;
+        break;
+      }
+      // the bucket's own key range for the next pass
+      uint32_t bmax = 0, bmin_inv = 0;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const bool c = (cand >> u) & 1u;
+        bmax = max(bmax, c ? kr[u] : 0u);
+        bmin_inv = max(bmin_inv, c ? ~kr[u] : 0u);
+      }
+      bmax = wave_max_u(bmax);
+      bmin_inv = wave_max_u(bmin_inv);
+      if (lane == 0) {
+        sh.red[1][wave] = bmax;
+        sh.red[2][wave] = bmin_inv;
+      }
+      for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+      __syncthreads();
+      hi = 0;
+      lo = 0xFFFFFFFFu;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        hi = max(hi, sh.red[1][w2]);
+        lo = min(lo, ~sh.red[2][w2]);
+      }
+      by_value = false;
+    }
+  }
+  if (mode == 1) {
+    // every candidate left has the same key: the first `remaining` in slot order
+    uint32_t m;
+    uint32_t pos = wg_excl_scan((uint32_t)__popc(cand), sh.scan_tot[1], &m);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if ((cand >> u) & 1u) keep |= (pos++ < remaining ? 1u : 0u) << u;
+  } else if (mode == 2) {
+    // at most kMaxCand candidates: gathered (any order), each ranked against
+    // all of them (key desc, slot asc); those ranked below `remaining` are kept
+    uint32_t* ckey = &sh.cand_key[0][0];
+    int32_t* cslot = &sh.cand_slot[0][0];
+    for (uint32_t bits = cand; bits != 0; bits &= bits - 1) {
+      const int u = __builtin_ctz(bits);
+      uint32_t k = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) k = i == u ? kr[i] : k;
+      const uint32_t slot = atomicAdd(&sh.n_cand, 1u);
+      ckey[slot] = k;
+      cslot[slot] = c0 + u;
+    }
+    __syncthreads();
+    if ((uint32_t)tid < in_bin) {
+      const uint32_t kt = ckey[tid];
+      const int ct = cslot[tid];
+      uint32_t rank = 0;
+      for (uint32_t j0 = 0; j0 < in_bin; j0 += 8) {  // 8 loads per LDS round trip
+        uint32_t k2[8];
+        int c2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          k2[i] = ckey[j0 + i];  // slots past in_bin (< kWaves * kMaxCand) are ignored
+          c2[i] = cslot[j0 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rank += (j0 + i < in_bin && (k2[i] > kt || (k2[i] == kt && c2[i] < ct))) ? 1u : 0u;
+      }
+      if (rank < remaining) atomicOr(&rbits[ct >> 5], 1u << (ct & 31));
+    }
+    __syncthreads();
+    keep |= rbits[tid];
+  }
+  // emission: kept candidates below the window in slot order, then the
+  // window's tokens [lo, T)
+  const int lo = p.window > 0 ? max(T - p.window, 0) : T;
+  // Slot c0 + u is token e * S + r with (e, r) = (e0, r0 + u) while
+  // r0 + u < S, else (e1, r0 + u - S) when S >= KPT (a thread's slots span
+  // at most two blocks); smaller S steps through the staged list.
+  // (Tokens of slots that hold none are computed but never stored.)
+  const int gi0 = c0 / S, r0 = c0 - gi0 * S, gmax = p.gamma_cap - 1;
+  const uint32_t e0 = (uint32_t)sh.gam[min(gi0, gmax)], e1 = (uint32_t)sh.gam[min(gi0 + 1, gmax)];
+  auto token_of = [&](int u) -> int {
+    if (S >= KPT) {  // uniform
+      const int r = r0 + u;
+      return (int)((r < S ? e0 : e1) * (uint32_t)S + (uint32_t)(r < S ? r : r - S));
+    }
+    const int q = (r0 + u) / S;
+    return (int)((uint32_t)sh.gam[min(gi0 + q, gmax)] * (uint32_t)S + (uint32_t)(r0 + u - q * S));
+  };
+  // bits u >= x (x clamped to [0, 32])
+  auto from_bit = [](int64_t x) -> uint32_t {
+    return x <= 0 ? 0xFFFFFFFFu : (x >= 32 ? 0u : 0xFFFFFFFFu << (int)x);
+  };
+  uint32_t in_window = 0;
+  if (S >= KPT) {  // uniform: two runs of consecutive tokens
+    const int64_t split = S - r0;  // first u in block e1
+    in_window = (from_bit(lo - ((int64_t)e0 * S + r0)) & ~from_bit(split)) |
+                (from_bit(split) & from_bit(split + lo - (int64_t)e1 * S));
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) in_window |= (token_of(u) >= lo ? 1u : 0u) << u;
+  }
+  const uint32_t rest = keep & ~in_window;
+  uint32_t total;
+  const uint32_t at = wg_excl_scan((uint32_t)__popc(rest), sh.scan_tot[2], &total);
+  const uint32_t cap = (uint32_t)p.out_cap;
+  int32_t* out = gids;
+  // position of kept slot u: at + the kept slots before it (no loop-carried
+  // state, so the 32 stores are independent predicated instructions)
+  auto store_all = [&](auto&& tok) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const uint32_t pos = at + (uint32_t)__popc(rest & ((1u << u) - 1u));
+      if (((rest >> u) & 1u) && pos < cap) out[pos] = tok(u);
+    }
+  };
+  if (S >= KPT)  // uniform
+    store_all([&](int u) {
+      const int r = r0 + u;
+      return (int)((r < S ? e0 : e1) * (uint32_t)S + (uint32_t)(r < S ? r : r - S));
+    });
+  else
+    store_all(token_of);
+  const int n_win = T - lo;
+  for (int i = tid; i < n_win; i += kThreads)
+    if (total + (uint32_t)i < cap) out[total + i] = lo + i;
+  if (tid == 0) *gcnt = (int)min(total + (uint32_t)n_win, cap);
+}
+
 // Top-k of a unit whose candidates fit in registers (n <= kThreads * kRegKeys):
 // thread t keeps the keys of candidates c = u * kThreads + t (u < kRegKeys),
 // so the published scores are read with coalesced loads and the histogram
@@ -539,30 +823,28 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
   constexpr int KPT = kRegKeys;
   const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
   const int n = ug.n;
-  if (n <= 0) {  // uniform
-    __syncthreads();
-    return;
-  }
+  // Score loads (coalesced) and the coarse entries bounded by the
+  // capacities, so that they do not wait for the unit's counts; slots past
+  // n are masked below.
   const float* sc = p.scores + (int64_t)unit * p.n_slots_max;  // published by the scoring
   float v[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u)  // unconditional (clamped), coalesced loads that overlap
-    v[u] = published(&sc[min(u * kThreads + tid, n - 1)]);
+    v[u] = published(&sc[min(u * kThreads + tid, p.n_slots_max - 1)]);
   // the block of each of this thread's candidates (-1: none). TWO: slot c is
   // offset c % ratio of coarse entry c / ratio; quotient and remainder are
-  // stepped from candidate to candidate (no division each), and the entries
-  // are loaded with the scores (gcnt >= 1 here, since n > 0).
+  // stepped from candidate to candidate (no division each).
   int blk[KPT];
+  int ent[KPT], gis[KPT], off[KPT];
   if (TWO) {
-    const int ratio = ug.slots.ratio, gc = ug.slots.gcnt;
+    const int ratio = p.ratio;
     const int dq = kThreads / ratio, dr = kThreads - dq * ratio;
     int gi = tid / ratio, r = tid - gi * ratio;
-    int ent[KPT], gis[KPT], off[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       gis[u] = gi;
       off[u] = r;
-      ent[u] = ug.slots.gamma[min(gi, gc - 1)];
+      ent[u] = ug.slots.gamma[min(gi, p.gamma_cap - 1)];
       gi += dq;
       r += dr;
       if (r >= ratio) {
@@ -570,6 +852,13 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
         ++gi;
       }
     }
+  }
+  if (n <= 0) {  // uniform
+    __syncthreads();
+    return;
+  }
+  if (TWO) {
+    const int gc = ug.slots.gcnt;
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
       blk[u] = u * kThreads + tid < n && gis[u] < gc ? ug.slots.from_entry(ent[u], off[u]) : -1;
@@ -984,11 +1273,13 @@ __device__ __forceinline__ int select_from_scores(const SelectParams& p, int uni
                                                   const UnitGeom& ug, TopkShared& sh,
                                                   uint32_t* dyn, int32_t* list, int32_t* gids,
                                                   int32_t* gcnt) {
-  if (!p.gamma && ug.n <= kThreads * kRegKeys)
+  // The path and the bitmap's extent follow the capacities, not the unit's
+  // counts, so that the score loads do not wait for the counts' loads.
+  if (!p.gamma && p.n_slots_max <= kThreads * kRegKeys)
     return topk_single(p, unit, ug, sh, list, gids, gcnt);
   uint32_t* bitmap = dyn;
-  for (int w = thread_id(); w < (ug.nb + 31) / 32; w += kThreads) bitmap[w] = 0u;
-  if (ug.n <= kThreads * kRegKeys) {
+  for (int w = thread_id(); w < (p.out_blocks_max + 31) / 32; w += kThreads) bitmap[w] = 0u;
+  if (p.gamma && p.n_slots_max <= kThreads * kRegKeys) {
     topk_regs<true>(p, unit, ug, sh, bitmap);
   } else {
     __syncthreads();
@@ -1032,10 +1323,13 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   // Slots map to blocks through coarse entries (two levels, token level):
   // the chunk's entries [g_lo, g_hi) are staged in LDS first (their loads
   // overlap the query loads below), so that no row load waits on a lookup.
+  // The staged range is bounded by the list's capacity, not its count, so
+  // these loads do not wait for the count's.
   const bool via_gamma = ug.slots.gamma != nullptr;  // uniform
   const int g_lo = via_gamma ? c_wg / p.ratio : 0;
-  const int g_hi = via_gamma ? min((c_wg + kRowsPerWG - 1) / p.ratio + 1, ug.slots.gcnt) : 0;
-  for (int i = tid; i < g_hi - g_lo; i += kThreads) sh.gam[i] = ug.slots.gamma[g_lo + i];
+  const int g_cap = via_gamma ? min((c_wg + kRowsPerWG - 1) / p.ratio + 1, p.gamma_cap) : 0;
+  const int g_hi = via_gamma ? min(g_cap, ug.slots.gcnt) : 0;
+  for (int i = tid; i < g_cap - g_lo; i += kThreads) sh.gam[i] = ug.slots.gamma[g_lo + i];
   auto block_of = [&](int c) {
     if (!via_gamma) return ug.slots.block_of(c);
     const int gi = c / p.ratio;
@@ -1099,21 +1393,9 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
       for (int u = 0; u < kUnroll; ++u) {
         const int c = cb + u * RPW + rg;
         if constexpr (kTok) {
-          int64_t off = -1;
-          if (p.tok_pages != nullptr) {
-            // the block's pages were resolved by launch_tok_pages: one load
-            // stands between the slot and its K row instead of two
-            if (c < c_end) {
-              const int gi = c / p.ratio, rr = c - gi * p.ratio, P = kv.page_size;
-              const int2 e = p.tok_pages[((int64_t)unit * p.gamma_cap + gi) * p.tok_ppb + rr / P];
-              if (rr % P < e.y)
-                off = (((int64_t)e.x * kv.num_kv_heads + g) * P + rr % P) *
-                      (int64_t)kv.head_dim * kv.elem_bytes;
-            }
-          } else {
-            const int beta = c < c_end ? block_of(c) : -1;
-            off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
-          }
+          // slot -> token through the staged block list, then its page
+          const int beta = c < c_end ? block_of(c) : -1;
+          const int64_t off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
           cs[u] = off >= 0 ? c : -1;
           r[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
                           : make_uint4(0, 0, 0, 0);
@@ -1209,6 +1491,13 @@ __device__ __forceinline__ void select_task(const SelectParams& p, int unit, int
                                             TopkShared& sh, uint32_t* dyn, int32_t* list) {
   score_chunk<TE, D, KIND, G>(p, unit, chunk, sh);
   if (!arrive_last(counter_of(p.counters, unit), nchunks, &sh.last)) return;
+  if constexpr (KIND == kKindTokens) {
+    if (p.n_slots_max <= kThreads * kTokKeys && p.gamma_cap <= kGammaLds) {  // uniform
+      topk_tokens(p, unit, unit_geom(p, unit), sh, p.out_ids + (int64_t)unit * p.out_cap,
+                  p.out_cnt + unit);
+      return;
+    }
+  }
   select_from_scores(p, unit, unit_geom(p, unit), sh, dyn, list,
                      p.out_ids + (int64_t)unit * p.out_cap, p.out_cnt + unit);
 }

@@ -77,7 +77,12 @@
 extern "C" {
 #endif
 
-#define HS_ATTN_VERSION 3
+#define HS_ATTN_VERSION 4
+
+/* Most dynamic LDS that hs_select_tokens uses above its register path (a
+ * bitmap of max_seq_len bits and the staged id list); with the kernel's own
+ * static LDS it stays within one gfx950 workgroup's 160 KiB. */
+#define HS_TOKEN_LDS_BYTES (120 << 10)
 
 /* Value of the status word of a fused-step workspace (hs_step_status) after
  * a call in which a workgroup's bounded wait for another expired. */
@@ -221,7 +226,9 @@ hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_n
  * the block selection, a finer pass keeps single tokens inside the chosen
  * blocks, for very high compression). For every unit, the candidates are the
  * tokens t < T_b of its selected blocks (block_ids / num_selected as written
- * by hs_select_blocks with block size `block_size`). Token score, fp32,
+ * by hs_select_blocks with block size `block_size`: ascending and distinct;
+ * for other lists the output is in list order and ties are broken by list
+ * position, but every access stays in bounds). Token score, fp32,
  * unscaled: sum over the unit's G query heads of q_j . k_t (the block score
  * of a one-token block). Kept, ascending, without duplicates: the first
  * min(top_k_tokens, #candidates) candidates by (score descending, token
@@ -234,11 +241,13 @@ hs_status hs_append_kv(const hs_kv_cache* kv, const void* k_new, const void* v_n
  * token_ids / num_tokens / max_tokens as its ids.
  * workspace: at least hs_select_tokens_workspace_size() bytes, 16-byte
  *   aligned and ZERO-FILLED before its first use; every call leaves its
- *   counters at zero. Requires k_pool. HS_ERR_UNSUPPORTED when the
- *   workgroup's LDS (a bitmap of max_seq_len bits, the candidates' keys and
- *   the id list) would exceed 64 KiB. When block_size is a multiple of the
- *   page size the call is two launches on the stream: one resolves the
- *   selected blocks' pages into the workspace, the other selects. */
+ *   counters at zero. Requires k_pool. One launch on the stream. Up to 8192
+ *   candidate slots (max_selected * block_size) and 512 selected blocks the
+ *   selection keeps its state in registers and needs no per-sequence LDS.
+ *   Above that it marks
+ *   kept tokens in an LDS bitmap of max_seq_len bits next to the staged id
+ *   list (max_tokens + 64 entries); HS_ERR_UNSUPPORTED when those would
+ *   exceed HS_TOKEN_LDS_BYTES. */
 hs_status hs_select_tokens_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
                                           int32_t block_size, int32_t max_selected,
                                           int32_t top_k_tokens, int32_t window_tokens,

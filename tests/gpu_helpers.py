@@ -223,3 +223,21 @@ def check_rows(w: Workload, got: np.ndarray, ref: np.ndarray, what="") -> float:
     assert err <= KERNEL_RTOL, "%s: max row rel err %.3g > kernel bound %.3g" % (
         what, err, KERNEL_RTOL)
     return err
+
+
+def check_tokens(gi, ref_ids, scores, kth, qo, K, T, W, what):
+    """Equal sizes; each (dropped, extra) pair of differing tokens is judged
+    by the near-tie rule on both members. Returns the number of pairs."""
+    g = gi.tolist()
+    assert g == sorted(set(g)), what
+    pairs = paired_differences(g, ref_ids.tolist(), what)
+    mag = np.abs(K[:T]) @ np.abs(qo).sum(axis=0)
+    for pair in pairs:
+        for t in pair:
+            assert not (t >= T - W), "%s: window token %d differs" % (what, t)
+            s = scores[t] if 0 <= t < T else float("nan")
+            assert not np.isnan(s), "%s: token %d was not a candidate" % (what, t)
+            tol = 1e-6 * max(abs(kth), mag[t])
+            assert abs(s - kth) <= tol, "%s: token %d (pair %s) score %.9g vs k-th %.9g" % (
+                what, t, pair, s, kth)
+    return len(pairs)

@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert hs.hs_version() == 3
+    assert hs.hs_version() == 4
 
 
 def test_step_status_rejects_bad_arguments():
@@ -275,3 +275,28 @@ def test_noalloc_step_refuses_before_any_hip_call():
     assert call(p, small, refresh=-1) == hs.HS_ERR_INVALID_ARG
     assert call(p, small, q=FAKE + 2) == hs.HS_ERR_INVALID_ARG
     assert call(hs.hs_select_params(32, 128, 512, 0, 10), small) == hs.HS_ERR_INVALID_ARG
+
+
+def test_token_stage_lds_cap():
+    """hs_select_tokens sizes its general path's LDS (a bitmap of max_seq_len
+    bits and the staged list of max_tokens + 64 entries) against
+    HS_TOKEN_LDS_BYTES: the largest capacity that fits is accepted, one token
+    more is refused, and the register path (at most 8192 slots and 512
+    blocks) needs no per-sequence LDS at any capacity."""
+    m = re.search(r"#define HS_TOKEN_LDS_BYTES \((\d+) << (\d+)\)", open(HEADER).read())
+    budget = int(m.group(1)) << int(m.group(2))
+    L = hs.lib()
+    size = ctypes.c_size_t(0)
+
+    def ws(max_seq_len, ms, S=32, kt=512, wt=64):
+        kv = kv_struct(batch=1, num_kv_heads=2, max_pages=-(-max_seq_len // 32),
+                       max_seq_len=max_seq_len)
+        max_tok = min(ms * S, kt) + wt
+        return L.hs_select_tokens_workspace_size(ctypes.byref(kv), 8, S, ms, kt, wt, max_tok,
+                                                 ctypes.byref(size))
+
+    cap = 32 * (budget // 4 - (512 + 64) - 64)  # 300 blocks: general path, 576 kept at most
+    assert ws(cap, 300) == hs.HS_OK
+    assert ws(cap + 1, 300) == hs.HS_ERR_UNSUPPORTED
+    assert ws(1 << 30, 200) == hs.HS_OK  # register path: 6400 slots, 200 blocks
+

@@ -7,10 +7,12 @@ those tokens. The oracle recomputes both from the same blocks. Token sets are
 bit-exact except for near ties: a token may differ only if its oracle score
 lies within 1e-6 * max(|s_k|, sum_j sum_i |q_j,i k_t,i|) of the k-th kept
 score s_k, and never inside the window. Every top-k path of the token level is
-covered: the register path (up to 4096 candidates), the general path with
-keys in LDS (up to 8192) and with keys in the workspace (more), and both forms
-of the id emission (compacted non-zero bitmap words, and the full scan of a
-dense bitmap).
+covered: the register path (at most 8192 candidate slots and 512 selected
+blocks; blocks of 32 tokens or more, and smaller blocks, several per thread),
+the general path with keys in LDS (at most 8192 slots but more blocks) and
+with keys in the workspace (more slots), and both forms of the general path's
+id emission (compacted non-zero bitmap words, and the full scan of a dense
+bitmap).
 """
 import numpy as np
 import pytest
@@ -18,7 +20,7 @@ import torch
 
 import hierarchical_sparse_attention_amd as hs
 import oracle
-from gpu_helpers import Problem, check_rows, log, paired_differences, unit_inputs
+from gpu_helpers import Problem, check_rows, check_tokens, log, unit_inputs
 from synth.workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -28,8 +30,12 @@ CASES = {
     # name: (workload, block top_k, token top_k, token window)
     "regs": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000), top_k=100),
              100, 256, 48),
-    "general-lds": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000),
-                                top_k=200), 200, 300, 0),
+    "regs-wide": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000),
+                              top_k=200), 200, 300, 0),
+    "regs-s16": (C[3].scaled(batch=2, hq=8, hkv=2, T=6001, seq_lens=(6001, 3100), S=16,
+                             page_size=16, top_k=150), 150, 400, 40),
+    "general-lds": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, S=8, page_size=8, top_k=600,
+                                window=64), 600, 700, 30),
     "general-ws": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, top_k=257), 257, 128, 64),
     "f32-box": (C[1].scaled(hq=4, hkv=2, d=128, T=2500, kind="minmax", S=32, page_size=32,
                             top_k=7), 7, 40, 20),
@@ -46,22 +52,15 @@ CASES = {
 _P = {}
 
 
-def check_tokens(gi, ref_ids, scores, kth, qo, K, T, W, what):
-    """Equal sizes; each (dropped, extra) pair of differing tokens is judged
-    by the near-tie rule on both members. Returns the number of pairs."""
-    g = gi.tolist()
-    assert g == sorted(set(g)), what
-    pairs = paired_differences(g, ref_ids.tolist(), what)
-    mag = np.abs(K[:T]) @ np.abs(qo).sum(axis=0)
-    for pair in pairs:
-        for t in pair:
-            assert not (t >= T - W), "%s: window token %d differs" % (what, t)
-            s = scores[t] if 0 <= t < T else float("nan")
-            assert not np.isnan(s), "%s: token %d was not a candidate" % (what, t)
-            tol = 1e-6 * max(abs(kth), mag[t])
-            assert abs(s - kth) <= tol, "%s: token %d (pair %s) score %.9g vs k-th %.9g" % (
-                what, t, pair, s, kth)
-    return len(pairs)
+# the top-k path each case must take
+PATHS = {"regs": "regs", "regs-wide": "regs", "regs-s16": "regs", "general-lds": "general",
+         "general-ws": "general", "f32-box": "regs", "d64-g8-pages": "regs", "mha-g1": "regs",
+         "dense-scan": "general"}
+
+
+def token_path(max_selected, S):
+    """The library's token top-k path for a list capacity and block size."""
+    return "regs" if max_selected * S <= 8192 and max_selected <= 512 else "general"
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -76,6 +75,7 @@ def test_token_stage_matches_oracle(name):
     summ = P.summaries()
     ids, cnt = P.select(q, summ, top_k=kb)
     ms = ids.shape[-1]
+    assert token_path(ms, w.S) == PATHS[name], (name, ms, w.S)
     max_tok = min(ms * w.S, kt) + min(wt, w.T)
     tok = torch.full((w.batch, w.hkv, max_tok), -7, dtype=torch.int32, device="cuda")
     tcnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
