@@ -307,6 +307,105 @@ __device__ __forceinline__ uint32_t take_digit_flat(TopkShared& sh, int nbins, i
   return bc.z;
 }
 
+// The float whose order_key is k (+0 for the key of -0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Threshold of a workgroup's top k_eff keys (0 < k_eff < n_valid) by buckets
+// over the candidates' own range. Thread t holds KPT keys kr (bit u of
+// `present`: kr[u] is a candidate; kmin / kmax: the candidates' extreme
+// keys). The first pass buckets linearly in value over [vmin, vmax] (rounded
+// float arithmetic is monotone, and the keys spread over all the buckets, so
+// the histogram's atomics rarely collide; a radix digit of the leading key
+// bits would put them in a few exponent buckets). While the threshold's
+// bucket holds more than kMaxCand candidates, the next pass buckets that
+// bucket's own [min, max] in key order (fixed-width buckets from its min),
+// which always splits it. Requires sh.hist[0, kBins) zero behind a barrier;
+// uses sh.red[1..2], sh.scan_tot[0] and sh.bcast.
+struct Threshold {
+  uint32_t keep;       // candidates above the threshold's bucket (or the whole bucket, taken)
+  uint32_t cand;       // the threshold bucket's candidates still to settle (modes 1, 2)
+  uint32_t remaining;  // how many of them are kept
+  uint32_t in_bin;     // their number over the workgroup
+  int mode;            // 0: settled, 1: all equal (first `remaining` in slot order), 2: rank
+};
+template <int KPT>
+__device__ __forceinline__ Threshold bucket_threshold(TopkShared& sh, const uint32_t (&kr)[KPT],
+                                                      uint32_t present, uint32_t k_eff,
+                                                      uint32_t n_valid, uint32_t kmin,
+                                                      uint32_t kmax) {
+  const int tid = thread_id(), lane = tid & (kWave - 1), wave = tid / kWave;
+  Threshold th{0u, present, k_eff, n_valid, 0};
+  uint32_t lo = kmin, hi = kmax;
+  const float vlo = key_value(lo), width = key_value(hi) - vlo;
+  const float vscale = (float)kBins / width;
+  bool by_value = width > 0.f && __builtin_isfinite(width) && __builtin_isfinite(vscale);
+  for (;;) {
+    if (lo == hi) {
+      th.mode = 1;
+      return th;
+    }
+    // this pass's bucket of every candidate (the dummy bin of the lane for
+    // the others); key buckets are (k - lo) >> sh_k with (hi - lo) >> sh_k
+    // in [kBins / 2, kBins)
+    const int sh_k = max(0, 32 - __clz(hi - lo) - kDigitBits);
+    uint32_t bk[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const uint32_t b = by_value
+          ? min((uint32_t)((key_value(kr[u]) - vlo) * vscale), (uint32_t)(kBins - 1))
+          : (kr[u] - lo) >> sh_k;
+      bk[u] = (th.cand >> u) & 1u ? b : (uint32_t)(kBins + lane);
+      atomicAdd(&sh.hist[bk[u]], 1u);
+    }
+    __syncthreads();
+    uint32_t d = 0;
+    th.in_bin = take_digit_flat(sh, kBins, 0, d, th.remaining);
+    uint32_t next = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {  // dummy bins are above every bucket but not candidates
+      const bool c = (th.cand >> u) & 1u;
+      th.keep |= (c && bk[u] > d ? 1u : 0u) << u;
+      next |= (c && bk[u] == d ? 1u : 0u) << u;
+    }
+    th.cand = next;
+    if (th.in_bin == th.remaining) {  // the whole bucket is kept
+      th.keep |= th.cand;
+      th.cand = 0;
+      return th;
+    }
+    if (th.in_bin <= (uint32_t)kMaxCand) {
+      th.mode = 2;
+      return th;
+    }
+    // the bucket's own key range for the next pass
+    uint32_t bmax = 0, bmin_inv = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool c = (th.cand >> u) & 1u;
+      bmax = max(bmax, c ? kr[u] : 0u);
+      bmin_inv = max(bmin_inv, c ? ~kr[u] : 0u);
+    }
+    bmax = wave_max_u(bmax);
+    bmin_inv = wave_max_u(bmin_inv);
+    if (lane == 0) {
+      sh.red[1][wave] = bmax;
+      sh.red[2][wave] = bmin_inv;
+    }
+    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
+    __syncthreads();
+    hi = 0;
+    lo = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      hi = max(hi, sh.red[1][w2]);
+      lo = min(lo, ~sh.red[2][w2]);
+    }
+    by_value = false;
+  }
+}
+
 // Top-k, window and ascending ids of a single-level unit with at most
 // kThreads * kRegKeys candidates (candidate c is block c), to `list` (LDS)
 // and/or `gids` / `*gcnt` (global). Thread t owns the contiguous candidates
@@ -395,85 +494,36 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
   const uint32_t kmin = ~kmin_inv;
   const uint32_t n_valid = n > 0 ? (uint32_t)n : 0u;
   const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
-  // threshold bin [prefix, pmax]: keys above it are kept, `remaining` of its
-  // in_bin keys are kept (ranked by key, then candidate index)
-  uint32_t prefix = 0xFFFFFFFFu, pmax = 0xFFFFFFFFu, remaining = 0, in_bin = 0;
-  int resolved = 32;
-  bool keep_all = false;
-  if (k_eff == n_valid && k_eff > 0) {
-    keep_all = true;
-  } else if (k_eff > 0) {
-    remaining = k_eff;
-    if (kmax == kmin) {
-      prefix = kmax;
-      in_bin = n_valid;
-    } else {
-      resolved = __clz(kmax ^ kmin);  // < 32 here
-      prefix = resolved == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> resolved));
-      for (bool first = true;; first = false) {
-        const int db = min(kDigitBits, 32 - resolved);
-        const int shift = 32 - resolved - db;
-        const uint32_t dmask = (1u << db) - 1u;
-        const uint32_t dummy = kBins + (tid & (kWave - 1));
-        if (first) {
-          // every present key shares the leading `resolved` bits: no test
-#pragma unroll
-          for (int u = 0; u < KPT; ++u)
-            atomicAdd(&sh.hist[kr[u] != 0 ? (kr[u] >> shift) & dmask : dummy], 1u);
-        } else {
-          const uint32_t hi_pre = prefix >> (32 - resolved);
-#pragma unroll
-          for (int u = 0; u < KPT; ++u) {
-            const bool in = kr[u] != 0 && (kr[u] >> (32 - resolved)) == hi_pre;
-            atomicAdd(&sh.hist[in ? (kr[u] >> shift) & dmask : dummy], 1u);
-          }
-        }
-        __syncthreads();
-        in_bin = take_digit_flat(sh, 1 << db, shift, prefix, remaining);
-        resolved += db;
-        if (in_bin == remaining || in_bin <= (uint32_t)kMaxCand || resolved == 32) break;
-        for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-        __syncthreads();
-      }
-    }
-    pmax = prefix | (resolved >= 32 ? 0u : (0xFFFFFFFFu >> resolved));
-  }
-  const bool take_bin = in_bin > 0 && in_bin == remaining;
-  const bool rank_bin = !keep_all && !take_bin && in_bin > 0;
-  // bit u of keep / inb: candidate c0 + u is kept / in the threshold bin.
-  // Present keys are never 0, so "present" is the candidate range alone, and
-  // prefix <= k <= pmax is one unsigned compare.
+  // bit u of keep / cand: candidate c0 + u is kept / in the threshold's
+  // bucket (present keys are never 0, so "present" is the candidate range)
   constexpr uint32_t kFull = (1u << KPT) - 1u;
   const auto from = [&](int lo) {  // bits u with c0 + u >= lo
     const int s = lo - c0;
     return s <= 0 ? kFull : (s >= KPT ? 0u : (kFull << s) & kFull);
   };
   const uint32_t present = kFull & ~from(n), in_window = from(w0);
-  uint32_t above = 0, in_range = 0;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    above |= (uint32_t)(kr[u] > pmax) << u;
-    in_range |= (uint32_t)(kr[u] - prefix <= pmax - prefix) << u;
-  }
-  uint32_t keep =
-      present & (keep_all ? kFull : (in_window | above | (take_bin ? in_range : 0u)));
+  const bool keep_all = k_eff > 0 && k_eff == n_valid;
+  Threshold th{0u, 0u, 0u, 0u, 0};
+  if (k_eff > 0 && !keep_all)  // uniform
+    th = bucket_threshold<KPT>(sh, kr, present, k_eff, n_valid, kmin, kmax);
+  uint32_t keep = present & (keep_all ? kFull : (in_window | th.keep));
   if (p.forced_cap > 0) {  // uniform
     __syncthreads();  // every forced bit is set
     keep |= (sh.kbits[c0 >> 5] >> (c0 & 31)) & kFull & present;
   }
-  const uint32_t inb = rank_bin ? in_range & present : 0u;
-  if (rank_bin && resolved == 32) {  // uniform
-    // every bin key equals the threshold: the first `remaining` of them in
+  const uint32_t inb = th.cand, remaining = th.remaining, in_bin = th.in_bin;
+  if (th.mode == 1) {  // uniform
+    // every key left equals the threshold: the first `remaining` of them in
     // candidate order are kept
     uint32_t m;
     uint32_t pos = wg_excl_scan((uint32_t)__popc(inb), sh.scan_tot[1], &m);
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
       if ((inb >> u) & 1u) keep |= (pos++ < remaining ? 1u : 0u) << u;
-  } else if (rank_bin) {  // uniform
-    // at most kMaxCand distinct-enough keys: gather them (any order), rank
-    // each against all of them (key desc, candidate asc) and set the bits of
-    // those ranked below `remaining`
+  } else if (th.mode == 2) {  // uniform
+    // at most kMaxCand keys: gather them (any order), rank each against all
+    // of them (key desc, candidate asc) and set the bits of those ranked
+    // below `remaining`
     uint32_t* ckey = &sh.cand_key[0][0];
     int32_t* cslot = &sh.cand_slot[0][0];
     for (uint32_t bits = inb; bits != 0; bits &= bits - 1) {  // usually no or one pass
@@ -539,10 +589,6 @@ __device__ __forceinline__ int topk_single(const SelectParams& p, int unit, cons
 // window in slot order, then the window's tokens. No bitmap over the
 // sequence is needed. Writes the ids and the count to gids / gcnt.
 constexpr int kTokKeys = 32;
-// The float whose order_key is k (+0 for the key of -0).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 static_assert(kThreads * kTokKeys / 32 <= kThreads * kRegKeys,
               "ranked-kept bits fit the transposition array");
 static_assert(kTokKeys == 32, "one word of keep bits per thread");
@@ -626,89 +672,17 @@ __device__ __forceinline__ void topk_tokens(const SelectParams& p, int unit, con
   }
   const uint32_t kmin = ~kmin_inv;
   const uint32_t k_eff = min((uint32_t)max(unit_top_k(p, ug.nb), 0), n_valid);
-  // Threshold by buckets over the candidates' own range. The first pass
-  // buckets linearly in value over [vmin, vmax] (rounded float arithmetic is
-  // monotone, and the keys spread over all the buckets, so the histogram's
-  // atomics rarely collide; a radix digit of the leading key bits would put
-  // them in a few exponent buckets). While the threshold's bucket holds more
-  // than kMaxCand candidates, the next pass buckets that bucket's own
-  // [min, max] in key order (fixed-width buckets from its min), which always
-  // splits it. Candidates above
-  // the threshold's bucket are kept; its own are ranked, or taken whole.
   const bool keep_all = k_eff > 0 && k_eff == n_valid;
   uint32_t keep = keep_all ? present : 0u;
-  uint32_t cand = 0, remaining = 0, in_bin = 0;  // cand: the threshold bucket's candidates
+  uint32_t cand = 0, remaining = 0, in_bin = 0;  // the threshold bucket's candidates to settle
   int mode = 0;                                  // 1: all equal, 2: rank (uniform)
   if (k_eff > 0 && !keep_all) {                  // uniform
-    remaining = k_eff;
-    cand = present;
-    in_bin = n_valid;
-    uint32_t lo = kmin, hi = kmax;
-    const float vlo = key_value(lo), width = key_value(hi) - vlo;
-    const float vscale = (float)kBins / width;
-    bool by_value = width > 0.f && __builtin_isfinite(width) && __builtin_isfinite(vscale);
-    for (;;) {
-      if (lo == hi) {
-        mode = 1;
-        break;
-      }
-      // this pass's bucket of every candidate (the dummy bin of the lane for
-      // the others); key buckets are (k - lo) >> sh_k with (hi - lo) >> sh_k
-      // in [kBins / 2, kBins)
-      const int sh_k = max(0, 32 - __clz(hi - lo) - kDigitBits);
-      uint32_t bk[KPT];
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const uint32_t b = by_value
-            ? min((uint32_t)((key_value(kr[u]) - vlo) * vscale), (uint32_t)(kBins - 1))
-            : (kr[u] - lo) >> sh_k;
-        bk[u] = (cand >> u) & 1u ? b : (uint32_t)(kBins + lane);
-        atomicAdd(&sh.hist[bk[u]], 1u);
-      }
-      __syncthreads();
-      uint32_t d = 0;
-      in_bin = take_digit_flat(sh, kBins, 0, d, remaining);
-      uint32_t next = 0;
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {  // dummy bins are above every bucket but not candidates
-        const bool c = (cand >> u) & 1u;
-        keep |= (c && bk[u] > d ? 1u : 0u) << u;
-        next |= (c && bk[u] == d ? 1u : 0u) << u;
-      }
-      cand = next;
-      if (in_bin == remaining) {  // the whole bucket is kept
-        keep |= cand;
-        break;
-      }
-      if (in_bin <= (uint32_t)kMaxCand) {
-        mode = 2;
-        break;
-      }
-      // the bucket's own key range for the next pass
-      uint32_t bmax = 0, bmin_inv = 0;
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const bool c = (cand >> u) & 1u;
-        bmax = max(bmax, c ? kr[u] : 0u);
-        bmin_inv = max(bmin_inv, c ? ~kr[u] : 0u);
-      }
-      bmax = wave_max_u(bmax);
-      bmin_inv = wave_max_u(bmin_inv);
-      if (lane == 0) {
-        sh.red[1][wave] = bmax;
-        sh.red[2][wave] = bmin_inv;
-      }
-      for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-      __syncthreads();
-      hi = 0;
-      lo = 0xFFFFFFFFu;
-#pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) {
-        hi = max(hi, sh.red[1][w2]);
-        lo = min(lo, ~sh.red[2][w2]);
-      }
-      by_value = false;
-    }
+    const Threshold th = bucket_threshold<KPT>(sh, kr, present, k_eff, n_valid, kmin, kmax);
+    keep = th.keep;
+    cand = th.cand;
+    remaining = th.remaining;
+    in_bin = th.in_bin;
+    mode = th.mode;
   }
   if (mode == 1) {
     // every candidate left has the same key: the first `remaining` in slot order
@@ -1297,7 +1271,8 @@ __device__ __forceinline__ int select_from_scores(const SelectParams& p, int uni
 // growing block), then scored from the stored rows with the same arithmetic
 // as every other row.
 // TS: storage type of a summary element (float for mean rows, TE for boxes).
-template <typename TE, int D, int KIND, int G>
+// UNR: rows in flight per lane group (kUnroll, or more where registers allow).
+template <typename TE, int D, int KIND, int G, int UNR = kUnroll>
 __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int chunk,
                                             TopkShared& sh) {
   constexpr bool kTok = KIND == kKindTokens;  // rows are token K rows (page table)
@@ -1386,30 +1361,31 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
                         (int64_t)unit * p.max_blocks * kRowBytes;
   if (c_begin < n_slots) {  // wave-uniform
     const int c_end = min(c_begin + kRowsPerWave, n_slots);
-    for (int cb = c_begin; cb < c_end; cb += RPW * kUnroll) {
-      uint4 r[kUnroll];
-      int cs[kUnroll];
+    static_assert(UNR <= 32, "one bit per row in flight");
+    for (int cb = c_begin; cb < c_end; cb += RPW * UNR) {
+      uint4 r[UNR];
+      uint32_t ok = 0;  // bit u: row cb + u * RPW + rg holds a candidate
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < UNR; ++u) {
         const int c = cb + u * RPW + rg;
         if constexpr (kTok) {
           // slot -> token through the staged block list, then its page
           const int beta = c < c_end ? block_of(c) : -1;
           const int64_t off = beta >= 0 ? row_offset(kv, b, g, beta) : -1;
-          cs[u] = off >= 0 ? c : -1;
+          ok |= (off >= 0 ? 1u : 0u) << u;
           r[u] = off >= 0 ? *reinterpret_cast<const uint4*>(kv.k_pool + off + li * 16)
                           : make_uint4(0, 0, 0, 0);
         } else {
           const int beta = c < c_end ? block_of(c) : -1;
-          cs[u] = beta >= 0 ? c : -1;
+          ok |= (beta >= 0 ? 1u : 0u) << u;
           r[u] = beta >= 0 ? *reinterpret_cast<const uint4*>(summ + beta * kRowBytes + li * 16)
                            : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < UNR; ++u) {
         const float acc = row_score(r[u]);
-        if (li == 0 && cs[u] >= 0) sh.stage[cs[u] - c_wg] = acc;
+        if (li == 0 && ((ok >> u) & 1u)) sh.stage[cb + u * RPW + rg - c_wg] = acc;
       }
     }
   }
