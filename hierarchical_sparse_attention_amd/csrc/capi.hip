@@ -196,11 +196,13 @@ hs_status check_step(const hs_select_params* p, const hs_kv_cache* kv, const hs_
 }
 
 // Selection parameters of the last level (the only one, or the fine level
-// of two); a two-level selection first launches its coarse level on s.
+// of two); a two-level selection first launches its coarse level on s, or,
+// with coarse_out, only returns that level's parameters there.
 hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, const void* q,
                         const hs_summaries* fine, const hs_summaries* coarse,
                         int32_t* block_ids, int32_t* num_selected, uint8_t* ws,
-                        const SelectLayout& L, hipStream_t s, hs::SelectParams* out) {
+                        const SelectLayout& L, hipStream_t s, hs::SelectParams* out,
+                        hs::SelectParams* coarse_out = nullptr) {
   int32_t* counters = reinterpret_cast<int32_t*>(ws + L.off_cnt);
   hs::SelectParams sp;
   sp.kv = view_of(kv);
@@ -233,8 +235,12 @@ hs_status select_params(const hs_select_params* prm, const hs_kv_cache* kv, cons
     sp.out_blocks_max = (int32_t)L.nc;
     sp.counters = counters + L.units * hs::kCounterStride;
     sp.refresh_begin = -1;
-    const hipError_t e = hs::launch_select(sp, s);
-    if (e != hipSuccess) return from_hip(e);
+    if (coarse_out) {
+      *coarse_out = sp;
+    } else {
+      const hipError_t e = hs::launch_select(sp, s);
+      if (e != hipSuccess) return from_hip(e);
+    }
   }
   sp.summ = fine->data;
   sp.kind = fine->kind;
@@ -530,19 +536,40 @@ hs_status select_decode(const hs_select_params* prm, const hs_kv_cache* kv, cons
   if (!isfinite(scale)) return HS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return HS_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (refresh_begin >= 0 && L.sel.two_level) {
-    // two levels: both tables are refreshed by the summary kernel first
-    hs_status r = hs_build_summaries(kv, refresh_begin, fine, s);
-    if (r != HS_OK) return r;
-    const int32_t cb = (int32_t)((int64_t)refresh_begin * fine->block_size / coarse->block_size);
-    r = hs_build_summaries(kv, cb, coarse, s);
-    if (r != HS_OK) return r;
-    refresh_begin = -1;
-  }
   hs::StepParams p;
-  st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected, ws + L.off_sel, L.sel, s,
-                     &p.sel);
-  if (st != HS_OK) return st;
+  if (refresh_begin >= 0 && L.sel.two_level) {
+    // two levels: both tables are refreshed before the coarse selection reads
+    // the coarse one; where the shapes allow, refreshes and coarse selection
+    // are one launch (the two-level head), else three
+    const int32_t cb = (int32_t)((int64_t)refresh_begin * fine->block_size / coarse->block_size);
+    hs::SelectParams cp;
+    st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected, ws + L.off_sel, L.sel,
+                       s, &p.sel, &cp);
+    if (st != HS_OK) return st;
+    if (hs::two_level_head_fits(cp, fine->block_size, coarse->kind)) {
+      hs::HeadParams h;
+      h.fine = fine->data;
+      h.fine_kind = fine->kind;
+      h.fine_block = fine->block_size;
+      h.fine_max_blocks = fine->max_blocks;
+      h.fine_begin = refresh_begin;
+      h.coarse_begin = cb;
+      const hipError_t e = hs::launch_two_level_head(cp, h, s);
+      if (e != hipSuccess) return from_hip(e);
+    } else {
+      hs_status r = hs_build_summaries(kv, refresh_begin, fine, s);
+      if (r != HS_OK) return r;
+      r = hs_build_summaries(kv, cb, coarse, s);
+      if (r != HS_OK) return r;
+      const hipError_t e = hs::launch_select(cp, s);
+      if (e != hipSuccess) return from_hip(e);
+    }
+    refresh_begin = -1;
+  } else {
+    st = select_params(prm, kv, q, fine, coarse, block_ids, num_selected, ws + L.off_sel, L.sel,
+                       s, &p.sel);
+    if (st != HS_OK) return st;
+  }
   p.dec = decode_params(kv, q, scale, fine->block_size, block_ids, num_selected,
                         prm->max_selected, out, ws + L.off_dec, L.dec);
   p.sel.refresh_begin = refresh_begin;

@@ -242,6 +242,20 @@ struct SelectParams {
   int32_t refresh_begin;     // >= 0: rebuild blocks from here on before scoring (single level)
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
+
+// Head of a two-level decode step, one launch: per unit (one workgroup), the
+// fine table's blocks from fine_begin are rebuilt (one wave each), then the
+// coarse table's blocks from coarse_begin (the whole workgroup each), then the
+// coarse selection runs on the refreshed table. `coarse` holds the coarse
+// level's selection parameters (its table is coarse.summ, of mean summaries,
+// and its candidates fit one scoring chunk).
+struct HeadParams {
+  void* fine;  // fine summary table
+  int32_t fine_kind, fine_block, fine_max_blocks, fine_begin;
+  int32_t coarse_begin;
+};
+bool two_level_head_fits(const SelectParams& coarse, int32_t fine_block, int32_t coarse_kind);
+hipError_t launch_two_level_head(const SelectParams& coarse, const HeadParams& h, hipStream_t s);
 // Dynamic LDS of a selection workgroup: bitmap words, then keys (general path).
 size_t select_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max);
 // Total dynamic LDS of a k_select launch (adds the staged id list).

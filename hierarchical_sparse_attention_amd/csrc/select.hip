@@ -22,6 +22,68 @@ __attribute__((amdgpu_waves_per_eu(KIND == kKindTokens ? 3 : 1))) void k_select(
 static_assert(sizeof(TopkShared) + HS_TOKEN_LDS_BYTES <= (160u << 10),
               "a token-level workgroup fits the LDS of a gfx950 workgroup");
 
+// Head of a two-level step (see HeadParams): refreshes, then the coarse
+// selection of the unit, whose candidates are one scoring chunk. The
+// rebuilt coarse rows are stored by this workgroup before its scoring loads
+// them (same compute unit and L2), so the scores see the new rows.
+constexpr int kHeadUnroll = 16;  // K loads in flight per lane while rebuilding
+template <typename TE, int D, int FKIND, int G>
+__global__ __launch_bounds__(kThreads) void k_two_level_head(SelectParams p, HeadParams h,
+                                                             int list_off) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  static_assert(kThreads == kSummWaves * kWave, "one workgroup builds a long block");
+  __shared__ union {
+    TopkShared t;
+    float seg[kSummWaves][2][D / EPL][EPL];
+  } sh;
+  extern __shared__ uint32_t dyn[];
+  const KvView& kv = p.kv;
+  const int unit = blockIdx.x;
+  const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
+  const int wave = thread_id() / kWave;
+  const int T = clamp_len(kv, b);
+  {  // fine blocks: one wave each
+    const int S = h.fine_block;
+    const int nb = min((T + S - 1) / S, h.fine_max_blocks);
+    for (int beta = h.fine_begin + wave; beta < nb; beta += kWaves)
+      summarize_block<TE, D, FKIND, kHeadUnroll>(kv, h.fine, (int64_t)unit * h.fine_max_blocks + beta,
+                                                 b, g, beta, S, T);
+  }
+  {  // coarse blocks: the whole workgroup each (uniform loop)
+    const int S = p.block_size;
+    const int nb = min((T + S - 1) / S, p.max_blocks);
+    for (int beta = h.coarse_begin; beta < nb; ++beta)
+      summarize_block_wg<TE, D, HS_SUMMARY_MEAN, kHeadUnroll>(
+          kv, const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + beta, b, g, beta, S, T,
+          sh.seg);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the rebuilt rows are stored
+  __syncthreads();
+  select_task<TE, D, HS_SUMMARY_MEAN, G>(p, unit, 0, 1, sh.t, dyn,
+                                         reinterpret_cast<int32_t*>(dyn + list_off));
+}
+
+template <typename TE, int D, int FKIND>
+hipError_t launch_head_g(const SelectParams& p, const HeadParams& h, size_t lds, int list_off,
+                         hipStream_t s) {
+  const dim3 grid(p.kv.batch * p.kv.num_kv_heads);
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 1>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
+    case 2: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 2>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
+    case 4: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 4>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
+    default: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 8>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename TE, int D>
+hipError_t launch_head_k(const SelectParams& p, const HeadParams& h, size_t lds, int list_off,
+                         hipStream_t s) {
+  return h.fine_kind == HS_SUMMARY_MEAN
+             ? launch_head_g<TE, D, HS_SUMMARY_MEAN>(p, h, lds, list_off, s)
+             : launch_head_g<TE, D, HS_SUMMARY_MINMAX>(p, h, lds, list_off, s);
+}
+
 template <typename TE, int D, int KIND, int G>
 hipError_t launch_one(const SelectParams& p, dim3 grid, size_t lds, int list_off, hipStream_t s) {
   const void* k = reinterpret_cast<const void*>(&k_select<TE, D, KIND, G>);
@@ -65,6 +127,24 @@ bool tokens_in_registers(int32_t kind, int32_t n_slots_max, int32_t gamma_cap) {
 
 size_t select_launch_lds_bytes(int32_t out_blocks_max, int32_t n_slots_max, int32_t out_cap) {
   return select_lds_bytes(out_blocks_max, n_slots_max) + sizeof(uint32_t) * ((size_t)out_cap + kWave);
+}
+
+bool two_level_head_fits(const SelectParams& coarse, int32_t fine_block, int32_t coarse_kind) {
+  return coarse_kind == HS_SUMMARY_MEAN && fine_block <= kSummSeg &&
+         select_chunks(coarse.n_slots_max) == 1 &&
+         select_launch_lds_bytes(coarse.out_blocks_max, coarse.n_slots_max, coarse.out_cap) <=
+             (48u << 10);
+}
+
+hipError_t launch_two_level_head(const SelectParams& p, const HeadParams& h, hipStream_t s) {
+  const int list_off = (int)(select_lds_bytes(p.out_blocks_max, p.n_slots_max) / sizeof(uint32_t));
+  const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.out_cap + kWave);
+  const bool bf = p.kv.elem_bytes == 2;
+  if (p.kv.head_dim == 64)
+    return bf ? launch_head_k<bf16_t, 64>(p, h, lds, list_off, s)
+              : launch_head_k<float, 64>(p, h, lds, list_off, s);
+  return bf ? launch_head_k<bf16_t, 128>(p, h, lds, list_off, s)
+            : launch_head_k<float, 128>(p, h, lds, list_off, s);
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {

@@ -156,6 +156,64 @@ __device__ __forceinline__ void summarize_block(const KvView& kv, void* out, int
   summ_store<TE, D, KIND>(out, row, acc0, acc1, t1 - t0);
 }
 
+// Waves of a workgroup that builds one long block together.
+constexpr int kSummWaves = 4;
+
+// summarize_block for one block by a whole workgroup of kSummWaves waves
+// (every thread calls it; blocks longer than a segment): in each round its
+// waves reduce the next kSummWaves segments side by side and wave 0 folds
+// them, in segment order, into the running values, so the row equals
+// summarize_block's. seg: LDS scratch of the workgroup.
+template <typename TE, int D, int KIND, int U>
+__device__ __forceinline__ void summarize_block_wg(
+    const KvView& kv, void* out, int64_t row, int b, int g, int beta, int S, int T,
+    float (*seg)[2][D / Vec16<TE>::EPL][Vec16<TE>::EPL]) {
+  constexpr int EPL = Vec16<TE>::EPL;
+  constexpr int LPT = D / EPL;
+  const int wave = thread_id() / kWave, lane = thread_id() & (kWave - 1);
+  const int t0 = beta * S, t1 = min(t0 + S, T);
+  const int nseg = (t1 - t0 + kSummSeg - 1) / kSummSeg;
+  float acc0[EPL], acc1[EPL];
+  for (int r = 0; r < nseg; r += kSummWaves) {
+    const int sg = r + wave;
+    if (sg < nseg) {
+      float s0[EPL], s1[EPL];
+      const int lo = t0 + sg * kSummSeg;
+      summ_segment<TE, D, KIND, U>(kv, b, g, lo, min(lo + kSummSeg, t1), s0, s1);
+      if (lane < LPT) {  // token group 0 holds the segment's values
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          seg[wave][0][lane][k] = s0[k];
+          seg[wave][1][lane][k] = s1[k];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int li = lane % LPT;
+      for (int w = 0; w < kSummWaves && r + w < nseg; ++w) {
+        float s0[EPL], s1[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          s0[k] = seg[w][0][li][k];
+          s1[k] = seg[w][1][li][k];
+        }
+        if (r + w == 0) {
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) {
+            acc0[k] = s0[k];
+            acc1[k] = s1[k];
+          }
+        } else {
+          summ_fold<TE, KIND>(acc0, acc1, s0, s1);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0) summ_store<TE, D, KIND>(out, row, acc0, acc1, t1 - t0);
+}
+
 // The same summary as summarize_block for a block of at most NL * TPW
 // tokens, in two steps so that the loads can be issued early and used later:
 // summ_load issues the block's K rows (NL 16-byte loads per lane, in the

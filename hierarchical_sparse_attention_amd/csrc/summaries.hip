@@ -28,65 +28,22 @@ __global__ __launch_bounds__(256) void k_build_summaries(SummParams p) {
                                              g, beta, S, T);
 }
 
-// Longer blocks: one workgroup per block. In each round its waves reduce the
-// next kWavesPerWG segments side by side and wave 0 folds them, in segment
-// order, into the running values, so the row equals summarize_block's.
+// Longer blocks: one workgroup per block (summarize_block_wg).
 template <typename TE, int D, int KIND>
 __global__ __launch_bounds__(256) void k_build_long_summaries(SummParams p) {
+  static_assert(kWavesPerWG == kSummWaves, "one block per workgroup of kSummWaves waves");
   constexpr int EPL = Vec16<TE>::EPL;
-  constexpr int LPT = D / EPL;
-  __shared__ float seg[kWavesPerWG][2][LPT][EPL];  // per wave: [sum or min, max][lane][dim]
+  __shared__ float seg[kSummWaves][2][D / EPL][EPL];  // per wave: [sum or min, max][lane][dim]
   const KvView& kv = p.kv;
   const int unit = blockIdx.y;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int S = p.block_size;
   const int beta = p.block_begin + blockIdx.x;
   const int T = clamp_len(kv, b);
   const int nb = (T + S - 1) / S;
   if (beta >= nb || beta >= p.max_blocks) return;  // uniform over the workgroup
-  const int t0 = beta * S, t1 = min(t0 + S, T);
-  const int nseg = (t1 - t0 + kSummSeg - 1) / kSummSeg;
-  float acc0[EPL], acc1[EPL];
-  for (int r = 0; r < nseg; r += kWavesPerWG) {
-    const int sg = r + wave;
-    if (sg < nseg) {
-      float s0[EPL], s1[EPL];
-      const int lo = t0 + sg * kSummSeg;
-      summ_segment<TE, D, KIND, kBuildUnroll>(kv, b, g, lo, min(lo + kSummSeg, t1), s0, s1);
-      if (lane < LPT) {  // token group 0 holds the segment's values
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) {
-          seg[wave][0][lane][k] = s0[k];
-          seg[wave][1][lane][k] = s1[k];
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int li = lane % LPT;
-      for (int w = 0; w < kWavesPerWG && r + w < nseg; ++w) {
-        float s0[EPL], s1[EPL];
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) {
-          s0[k] = seg[w][0][li][k];
-          s1[k] = seg[w][1][li][k];
-        }
-        if (r + w == 0) {
-#pragma unroll
-          for (int k = 0; k < EPL; ++k) {
-            acc0[k] = s0[k];
-            acc1[k] = s1[k];
-          }
-        } else {
-          summ_fold<TE, KIND>(acc0, acc1, s0, s1);
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (wave == 0)
-    summ_store<TE, D, KIND>(p.out, (int64_t)unit * p.max_blocks + beta, acc0, acc1, t1 - t0);
+  summarize_block_wg<TE, D, KIND, kBuildUnroll>(kv, p.out, (int64_t)unit * p.max_blocks + beta,
+                                                b, g, beta, S, T, seg);
 }
 
 template <typename TE, int D>
