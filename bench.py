@@ -92,6 +92,9 @@ KERNEL_SOURCES = {
     "hs_select_blocks": [_CSRC + f for f in ("select.hip", "select_impl.h", "hs_internal.h")],
     "hs_decode_step": [_CSRC + f for f in ("step.hip", "select_impl.h", "decode_impl.h",
                                            "summ_impl.h", "hs_internal.h")],
+    # two levels: the launch before the fused kernel (refreshes + coarse selection)
+    "hs_two_level_head": [_CSRC + f for f in ("select.hip", "select_impl.h", "summ_impl.h",
+                                              "hs_internal.h")],
     # token level: the selection kernel with token rows, and the token-list attention
     "hs_select_tokens": [_CSRC + f for f in ("select.hip", "select_impl.h", "hs_internal.h")],
     "hs_sparse_decode_tokens": [_CSRC + f for f in ("decode.hip", "decode_impl.h",
@@ -644,6 +647,7 @@ def config_figure(w, stream, reps, calls=8):
            "GBps": nb["step"] / (ms * 1e-3) / 1e9,
            "frac": nb["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "traffic": dominant_traffic(w, nb),
+           "head_traffic": measured_traffic("hs_two_level_head", w.name) if kc else None,
            "mean_selected": float(hc.mean()), "needle_recall": needle_recall(w, hi, hc),
            "cache_resident": work < (256 << 20)}
     log("figure %s: %.4f ms per step, %.0f GB/s (%.3f of peak), needle recall %s" % (
