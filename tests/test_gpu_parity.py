@@ -28,6 +28,10 @@ SMALL = {
     "c4s": C[4].scaled(batch=2, hq=2, hkv=2, T=16684, top_k=16, top_k_coarse=4,
                        seq_lens=(16684, 9000)),
     "c5s": C[5].scaled(batch=2, hq=8, hkv=2, T=4160, top_k=6, layers=3),
+    # two levels over box (min/max) fine summaries, fp32, GQA, d 64
+    "c4s-box-f32-g4": C[4].scaled(batch=2, hq=8, hkv=2, d=64, T=9000, dtype="f32", kind="minmax",
+                                  S=32, page_size=32, coarse_S=512, top_k=24, top_k_coarse=6,
+                                  window=128, needles=0, seq_lens=(9000, 4100)),
     "g8-d64-mean": C[3].scaled(batch=2, hq=16, hkv=2, d=64, T=3001, kind="mean", S=64,
                                page_size=16, top_k=5, window=100, needles=0,
                                seq_lens=(3001, 1500)),
