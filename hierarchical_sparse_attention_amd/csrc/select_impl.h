@@ -16,15 +16,16 @@
 //    element costs one FMA whatever G is. A row is read by LPR lanes with
 //    16-byte loads and reduced across them with DPP; fp32 scores go to the
 //    workspace with device-coherent stores.
-//  * top-k - one workgroup reads the unit's published scores and selects.
-//    Exact radix select on order-preserving uint32 keys of the fp32 scores:
-//    the leading bits shared by every key are skipped and the next 11-bit
-//    digit is resolved with an LDS histogram; this usually narrows the k-th
-//    largest key to a bin of a few keys, which are then ranked directly
-//    (key descending, candidate index ascending: the lowest-index
-//    tie-break); a crowded bin takes further 11-bit passes. Kept blocks and
-//    the window's blocks are set in an LDS bitmap and written out as
-//    ascending ids (to LDS, to global memory, or both).
+//  * top-k - one workgroup reads the unit's published scores and selects,
+//    exactly, on order-preserving uint32 keys of the fp32 scores. With the
+//    keys in registers (every path up to 4096 block candidates or 8192
+//    token slots) an LDS histogram over the candidates' own value range
+//    narrows the k-th largest key to a bucket, usually of a few keys, which
+//    are then ranked directly (key descending, candidate index ascending:
+//    the lowest-index tie-break); a crowded bucket is split again over its
+//    own key range. Larger units take 11-bit radix passes over keys in LDS
+//    or re-read from the scores. Kept blocks and the window's blocks are
+//    written out as ascending ids (to LDS, to global memory, or both).
 #pragma once
 
 #include <type_traits>
@@ -880,62 +881,33 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
       if (kr[u]) mark(bitmap, blk[u]);
     return;
   }
-  // Threshold: after the loop every key > pmax is kept, every key < prefix is
-  // dropped, and `remaining` of the in_bin keys in [prefix, pmax] are kept.
-  uint32_t prefix, remaining = k_eff, in_bin;
-  int resolved;  // leading key bits fixed in prefix
-  if (kmax == kmin) {
-    prefix = kmax;
-    resolved = 32;
-    in_bin = n_valid;
-  } else {
-    resolved = __clz(kmax ^ kmin);  // < 32 here
-    prefix = resolved == 0 ? 0u : (kmax & ~(0xFFFFFFFFu >> resolved));
-    for (;;) {
-      const int db = min(kDigitBits, 32 - resolved);
-      const int shift = 32 - resolved - db;
-      const uint32_t dmask = (1u << db) - 1u;
+  uint32_t present = 0;
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const uint32_t k = kr[u];
-        if (k != 0 && (resolved == 0 || (k >> (32 - resolved)) == (prefix >> (32 - resolved))))
-          atomicAdd(&sh.hist[hist_slot((k >> shift) & dmask)], 1u);
-      }
-      __syncthreads();
-      in_bin = take_digit(sh, 1 << db, shift, prefix, remaining);
-      resolved += db;
-      if (in_bin == remaining || in_bin <= (uint32_t)kMaxCand || resolved == 32) break;
-      for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-      __syncthreads();
-    }
-  }
-  const uint32_t pmax = prefix | (resolved >= 32 ? 0u : (0xFFFFFFFFu >> resolved));
-  const bool take_bin = in_bin == remaining;
-  const bool rank_bin = !take_bin && in_bin <= (uint32_t)kMaxCand;
+  for (int u = 0; u < KPT; ++u) present |= (blk[u] >= 0 ? 1u : 0u) << u;
+  const Threshold th = bucket_threshold<KPT>(sh, kr, present, k_eff, n_valid, kmin, kmax);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if ((th.keep >> u) & 1u) mark(bitmap, blk[u]);
+  const uint32_t remaining = th.remaining;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  // keys above the bin (and the whole bin when all of it is kept) are marked;
-  // the bin's keys are gathered per wave with ballots for the ranking
-  uint32_t wrun = 0;
+  if (th.mode == 2) {  // uniform
+    // at most kMaxCand keys left: gathered per wave with ballots, each ranked
+    // against all of them (key desc, candidate asc)
+    uint32_t wrun = 0;
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const uint32_t k = kr[u];
-    const bool inb = k != 0 && k >= prefix && k <= pmax;
-    if (k > pmax || (take_bin && inb)) mark(bitmap, blk[u]);
-    if (rank_bin) {
+    for (int u = 0; u < KPT; ++u) {
+      const bool inb = (th.cand >> u) & 1u;
       const uint64_t m = __ballot(inb);
       if (inb) {
         const uint32_t pos = wrun + (uint32_t)__popcll(m & below);
-        sh.cand_key[wave][pos] = k;
+        sh.cand_key[wave][pos] = kr[u];
         sh.cand_slot[wave][pos] = u * kThreads + tid;
         sh.cand_blk[wave][pos] = blk[u];
       }
       wrun += (uint32_t)__popcll(m);
     }
-  }
-  if (rank_bin) {
     if (lane == 0) sh.wcnt[wave] = wrun;
     __syncthreads();
-    // rank of a bin key = bin keys before it in (key desc, candidate asc) order
     uint32_t wc[kWaves], first = 0;
     int w = -1;
 #pragma unroll
@@ -964,15 +936,14 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
         }
       if (rank < remaining) mark(bitmap, bt);
     }
-  } else if (!take_bin) {
-    // more than kMaxCand keys all equal to the threshold: the first
-    // `remaining` of them in candidate order are kept. Rank of a tie = ties
-    // at earlier slots, then at earlier waves of the same slot, then at lower
-    // lanes.
+  } else if (th.mode == 1) {  // uniform
+    // more than kMaxCand keys, all equal: the first `remaining` of them in
+    // candidate order are kept. Rank of a tie = ties at earlier slots, then
+    // at earlier waves of the same slot, then at lower lanes.
     uint64_t tie_mask[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      tie_mask[u] = __ballot(kr[u] != 0 && kr[u] == prefix);
+      tie_mask[u] = __ballot((th.cand >> u) & 1u);
       if (lane == 0) sh.tie_cnt[u][wave] = (uint32_t)__popcll(tie_mask[u]);
     }
     __syncthreads();
@@ -986,7 +957,7 @@ __device__ __forceinline__ void topk_regs(const SelectParams& p, int unit, const
         in_slot += cw;
         waves_before += w2 < wave ? cw : 0u;
       }
-      if (kr[u] != 0 && kr[u] == prefix &&
+      if (((th.cand >> u) & 1u) &&
           before + waves_before + (uint32_t)__popcll(tie_mask[u] & below) < remaining)
         mark(bitmap, blk[u]);
       before += in_slot;
