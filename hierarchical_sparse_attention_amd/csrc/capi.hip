@@ -172,6 +172,14 @@ hs_status check_decode(const hs_kv_cache* kv, int32_t num_q_heads, int32_t block
 
 hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
 
+// The separate decode launch keeps each split task's run of the list in LDS.
+hs_status check_decode_run(const hs_kv_cache* kv, int32_t block_size, int32_t max_selected,
+                           const DecodeLayout& L) {
+  const size_t run = hs::decode_run_bytes(kv->dtype == HS_BF16 ? 2 : 4, block_size, max_selected,
+                                          (int)L.n_splits);
+  return run <= hs::kDecodeRunLds ? HS_OK : HS_ERR_INVALID_ARG;
+}
+
 // Workspace of hs_select_decode: [control words][selection workspace][decode
 // workspace].
 struct StepLayout {
@@ -415,7 +423,8 @@ hs_status hs_decode_workspace_size(const hs_kv_cache* kv, int32_t num_q_heads,
                                    int32_t block_size, int32_t max_selected, size_t* bytes) {
   if (!bytes) return HS_ERR_INVALID_ARG;
   DecodeLayout L;
-  const hs_status st = check_decode(kv, num_q_heads, block_size, max_selected, &L);
+  hs_status st = check_decode(kv, num_q_heads, block_size, max_selected, &L);
+  if (st == HS_OK) st = check_decode_run(kv, block_size, max_selected, L);
   if (st == HS_OK) *bytes = L.total;
   return st;
 }
@@ -501,6 +510,7 @@ hs_status hs_sparse_decode(const hs_kv_cache* kv, const void* q, int32_t num_q_h
                            void* workspace, size_t workspace_bytes, void* stream) {
   DecodeLayout L;
   hs_status st = check_decode(kv, num_q_heads, block_size, max_selected, &L);
+  if (st == HS_OK) st = check_decode_run(kv, block_size, max_selected, L);
   if (st != HS_OK) return st;
   if (!q || !aligned16(q) || !block_ids || !num_selected || !out) return HS_ERR_INVALID_ARG;
   if (!isfinite(scale)) return HS_ERR_INVALID_ARG;

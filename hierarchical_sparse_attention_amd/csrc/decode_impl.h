@@ -175,10 +175,13 @@ struct DecodeShared {
 
 // Attention of the unit's query heads over the blocks ids[e0 .. e1) (a list
 // in LDS or global memory) of a bf16 cache; leaves each wave's state in
-// ds.sh for finish_split. TOK: the ids are single tokens (block size 1).
+// ds.sh for finish_split. TOK: the list is of single tokens (block size 1),
+// given as the byte offsets of their rows, rows[e0 .. e1) (-1: masked),
+// resolved by the caller.
 template <int D, int G, bool TOK>
 __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, const int32_t* ids,
-                                            int e0, int e1, DecodeShared<D, G>& ds) {
+                                            int e0, int e1, DecodeShared<D, G>& ds,
+                                            const int64_t* rows) {
   constexpr int KC = D / 32;       // MFMA k-chunks per token row
   constexpr int VL = D / 8;        // lanes per V row (16 bytes each)
   constexpr int TPV = kWave / VL;  // tokens per V load instruction
@@ -207,9 +210,9 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // multiples of 32: then one page lookup serves the whole stage
   const bool whole_page = (kv.page_size % 32 == 0) && (S % 32 == 0);
   // block size 1 (a token list, e.g. from the token-level second stage): a
-  // stage is up to 32 consecutive list entries, each lane looks up its own
-  // token's row; tokens outside [0, T) or on an absent page are masked (their
-  // lanes read row 0 of the sequence, whose values are finite)
+  // stage is up to 32 consecutive list entries, each lane reads its own
+  // token's row offset from `rows`; masked tokens (outside [0, T) or on an
+  // absent page) read row 0 of the sequence, whose values are finite
   constexpr bool tok_list = TOK;
   const int64_t row_bytes = (int64_t)D * EB;
 
@@ -243,8 +246,7 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   const int64_t row0 = T > 0 ? max(row_offset(kv, b, g, 0), (int64_t)0) : 0;
   // byte offset of the row of list entry `e` (token list mode) and its validity
   auto token_row = [&](int e, bool& valid) {
-    const int t = ids[e];
-    int64_t off = (unsigned)t < (unsigned)T ? row_offset(kv, b, g, t) : -1;
+    const int64_t off = rows[e];
     valid = off >= 0;
     return valid ? off : row0;
   };
@@ -559,12 +561,14 @@ constexpr int f32_unroll() { return G == 8 ? 4 : 8; }
 
 // Attention of one split task over ids[e0 .. e1), then its partial and
 // arrival (the last task of the unit merges).
-// TOK: the ids are single tokens (block size 1; see attend_bf16).
+// TOK: single tokens given by their row offsets rows[e0 .. e1) (block size
+// 1; see attend_bf16).
 template <typename TE, int D, int G, bool TOK = false>
 __device__ __forceinline__ void decode_split(const DecodeParams& p, int unit, int split,
                                              const int32_t* ids, int e0, int e1,
-                                             DecodeShared<D, G>& ds) {
-  if constexpr (sizeof(TE) == 2) attend_bf16<D, G, TOK>(p, unit, ids, e0, e1, ds);
+                                             DecodeShared<D, G>& ds,
+                                             const int64_t* rows = nullptr) {
+  if constexpr (sizeof(TE) == 2) attend_bf16<D, G, TOK>(p, unit, ids, e0, e1, ds, rows);
   else attend_f32<D, G, f32_unroll<G>()>(p, unit, ids, e0, e1, ds);
   finish_split<D, G>(p, ds.sh, unit, split);
 }

@@ -289,6 +289,15 @@ constexpr int kMaxSplits = 128;
 // compute unit keeps more KV loads in flight), at most one per selectable
 // block and at most kMaxSplits.
 int decode_splits(int64_t units, int32_t max_selected, int32_t block_size);
+// LDS of the run of the list that one split task of the separate decode
+// launch holds: int32 ids, or int64 row offsets for the token lists (block
+// size 1) of a bf16 cache; larger runs are refused before the launch.
+constexpr size_t kDecodeRunLds = 96u << 10;
+inline size_t decode_run_bytes(int elem_bytes, int32_t block_size, int32_t max_selected,
+                               int n_splits) {
+  const size_t per = elem_bytes == 2 && block_size == 1 ? sizeof(int64_t) : sizeof(int32_t);
+  return per * (size_t)((max_selected + n_splits - 1) / n_splits);
+}
 
 // Control line of the fused launch at the start of its workspace (int32
 // index of the status word the host reads; the line is 256 bytes).

@@ -348,6 +348,12 @@ hs_status hs_select_blocks(const hs_select_params* p, const hs_kv_cache* kv,
  * selection, [SparDA 3.4]); they are only read. Ids outside
  * [0, ceil(T_b / S)) are skipped. Ids of one unit must be distinct
  * (hs_select_blocks guarantees it); an id listed twice is attended twice.
+ * A unit's list is cut into n split tasks (n = ceil(256 / units), or
+ * ceil(512 / units) when max_selected * S >= 2048 * ceil(256 / units); then
+ * at most max_selected and 128), each holding ceil(max_selected / n) entries
+ * in LDS, 4 bytes each (8 for S = 1 on a bf16 cache), at most 96 KiB:
+ * larger lists return HS_ERR_INVALID_ARG (here and from
+ * hs_decode_workspace_size).
  * workspace: device buffer of at least hs_decode_workspace_size() bytes,
  *   16-byte aligned and ZERO-FILLED before its first use. It starts with
  *   per-unit arrival counters (the last split of a unit to finish merges the

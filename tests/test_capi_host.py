@@ -92,6 +92,28 @@ def test_decode_split_count_follows_the_work_per_split():
     assert dsize(kv, 64, 73) - dsize(kv, 1, 73) == 256 * 1 * (128 + 2) * 4
 
 
+def test_decode_rejects_runs_beyond_the_lds_of_a_split_task():
+    """A split task of hs_sparse_decode holds its run of the list in LDS, at
+    most 96 KiB: 4-byte ids, 8-byte row offsets for token lists (S = 1) of a
+    bf16 cache. 32 units take 16 splits at these lengths."""
+    def st(kv, block_size, max_selected):
+        n = ctypes.c_size_t(0)
+        return hs.lib().hs_decode_workspace_size(ctypes.byref(kv), 32, block_size, max_selected,
+                                                 ctypes.byref(n))
+    kv = kv_struct()
+    assert st(kv, 1, 16 * 12288) == hs.HS_OK          # 12288 tokens x 8 B per split
+    assert st(kv, 1, 16 * 12288 + 1) == hs.HS_ERR_INVALID_ARG
+    assert st(kv, 32, 16 * 24576) == hs.HS_OK         # 24576 ids x 4 B per split
+    assert st(kv, 32, 16 * 24576 + 1) == hs.HS_ERR_INVALID_ARG
+    kv32 = kv_struct(dtype=hs.HS_F32)
+    assert st(kv32, 1, 16 * 24576) == hs.HS_OK        # float32 caches keep the ids
+    assert st(kv32, 1, 16 * 24576 + 1) == hs.HS_ERR_INVALID_ARG
+    # the entry point refuses it before any launch
+    assert hs.lib().hs_sparse_decode(ctypes.byref(kv), FAKE, 32, ctypes.c_float(0.0), 1, FAKE,
+                                     FAKE, 16 * 12288 + 1, FAKE, FAKE, 1 << 40, None) == \
+        hs.HS_ERR_INVALID_ARG
+
+
 def test_select_workspace_size_layout():
     p = hs.hs_select_params(32, 128, 512, 0, 145)
     st, n = sel_size(p, kv_struct(), summ())
