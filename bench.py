@@ -332,16 +332,8 @@ def main():
             for c in copies:
                 c["calls"][j]()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.event_steps)]
-        with torch.cuda.stream(stream):
-            g.replay()
-            for e0, e1 in evs:
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        call_ms.append(float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(copies))
+        replay_t = replay_ms(g, stream, args.event_steps)
+        call_ms.append(float(replay_t.mean()) / len(copies))
         del g
     call_ms = np.array(call_ms)
     log("per-call mean ms: refresh %.4f select %.4f decode %.4f select+decode %.4f step %.4f" %
@@ -541,10 +533,30 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def replay_ms(g, stream, reps, inner=4):
+    """Per-replay ms of graph `g` on `stream`, one figure per event pair: `reps`
+    event pairs, each around `inner` back-to-back replays (so that the host's
+    event and launch work overlaps the GPU's rather than adding to short
+    replays), after one untimed replay."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        g.replay()
+        for e0, e1 in evs:
+            e0.record(stream)
+            for _ in range(inner):
+                g.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in evs]) / inner
+
+
 def timed_graph(body, stream, reps):
     """Mean ms of one replay of a graph captured from body(), over `reps`
-    event-timed replays on `stream` after one untimed replay, and the
-    per-replay times."""
+    event-timed groups of replays on `stream` after one untimed replay, and
+    the per-replay times."""
     import numpy as np
     import torch
     with torch.cuda.stream(stream):
@@ -554,16 +566,7 @@ def timed_graph(body, stream, reps):
     with torch.cuda.graph(g, stream=stream):
         body()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    with torch.cuda.stream(stream):
-        g.replay()
-        for e0, e1 in evs:
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-    torch.cuda.synchronize()
-    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    t = replay_ms(g, stream, reps)
     del g
     return float(t.mean()), t
 
@@ -694,16 +697,8 @@ def decode_loop(w, c, pt, stream, reps, steps=64):
         with torch.cuda.graph(g, stream=stream):
             body(with_step)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        with torch.cuda.stream(stream):
-            g.replay()
-            for e0, e1 in evs:
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        out[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / steps
+        replay_t = replay_ms(g, stream, reps)
+        out[name] = float(replay_t.mean()) / steps
         del g
     assert sl.cpu().tolist() == [w.T] * w.batch
     return {"steps_per_loop": steps, "start_len": t0, "ms_per_step": out["loop"],
@@ -750,16 +745,8 @@ def schedule_timing(w, copies, stream, reps, reserve=0.01):
         for call in calls:
             call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    with torch.cuda.stream(stream):
-        g.replay()
-        for e0, e1 in evs:
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(calls)
+    replay_t = replay_ms(g, stream, reps)
+    ms = float(replay_t.mean()) / len(calls)
     ids, cnt = bufs[0][0].cpu().numpy(), bufs[0][1].cpu().numpy()
     lens = w.seq_lens_array()
     esize = 2 if w.dtype == "bf16" else 4
@@ -810,16 +797,8 @@ def token_stage_timing(w, copies, stream, reps, k_tok=1024, window=512):
             for call in calls:
                 call()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        with torch.cuda.stream(stream):
-            g.replay()
-            for e0, e1 in evs:
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(calls)
+        replay_t = replay_ms(g, stream, reps)
+        res[name] = float(replay_t.mean()) / len(calls)
         del g
     esize = 2 if w.dtype == "bf16" else 4
     cnt = copies[0]["cnt"].cpu().numpy()
@@ -879,16 +858,8 @@ def block_cache_timing(w, stream, reps, steps=16, keep=0.85):
             hs.hs_block_cache_update(cache, t, d_ids[t], d_cnt[t], slot_of, miss, stats[t],
                                      stream=stream)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    with torch.cuda.stream(stream):
-        g.replay()
-        for e0, e1 in evs:
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-    torch.cuda.synchronize()
-    ms_call = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / steps
+    replay_t = replay_ms(g, stream, reps)
+    ms_call = float(replay_t.mean()) / steps
     st = stats.cpu().numpy()[1:]  # steps after the first (cold) one
     return {"capacity": 4 * ms, "units": units, "steps": steps, "ms_per_call": ms_call,
             "mean_overlap": float(1.0 - st[:, :, 2].sum() / st[:, :, :2].sum()),
@@ -970,16 +941,8 @@ def shared_selection_timing(stream, reps):
         with torch.cuda.graph(g, stream=stream):
             body()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        with torch.cuda.stream(stream):
-            g.replay()
-            for e0, e1 in evs:
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        replay_t = replay_ms(g, stream, reps)
+        ms = float(replay_t.mean())
         del g
         if name == "shared":
             b0 = decode_bytes(L0["ids"].cpu().numpy(), L0["cnt"].cpu().numpy())
