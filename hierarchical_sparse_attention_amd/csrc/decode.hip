@@ -29,10 +29,15 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
     const KvView& kv = p.kv;
     const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
     const int T = clamp_len(kv, b);
+    // a masked token (outside [0, T) or on an absent page) is stored as ~r,
+    // r the offset of row 0 of the sequence (finite values), which its lane
+    // reads instead; its page is looked up here, beside the list's
+    const int64_t r0 = T > 0 ? max(row_offset(kv, b, g, 0), (int64_t)0) : 0;
     int64_t* rows = dyn_lds;
     for (int i = thread_id(); i < e1 - e0; i += kDecThreads) {
       const int t = ids[e0 + i];
-      rows[i] = (unsigned)t < (unsigned)T ? row_offset(kv, b, g, t) : -1;
+      const int64_t off = (unsigned)t < (unsigned)T ? row_offset(kv, b, g, t) : -1;
+      rows[i] = off >= 0 ? off : ~r0;
     }
     __syncthreads();
     decode_split<TE, D, G, true>(p, unit, split, nullptr, 0, e1 - e0, ds, rows);

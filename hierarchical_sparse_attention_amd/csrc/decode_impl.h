@@ -176,8 +176,9 @@ struct DecodeShared {
 // Attention of the unit's query heads over the blocks ids[e0 .. e1) (a list
 // in LDS or global memory) of a bf16 cache; leaves each wave's state in
 // ds.sh for finish_split. TOK: the list is of single tokens (block size 1),
-// given as the byte offsets of their rows, rows[e0 .. e1) (-1: masked),
-// resolved by the caller.
+// given as the byte offsets of their rows, rows[e0 .. e1), resolved by the
+// caller; a masked token's entry is ~r, r the offset of a finite row its
+// lane reads instead.
 template <int D, int G, bool TOK>
 __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, const int32_t* ids,
                                             int e0, int e1, DecodeShared<D, G>& ds,
@@ -212,7 +213,7 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // block size 1 (a token list, e.g. from the token-level second stage): a
   // stage is up to 32 consecutive list entries, each lane reads its own
   // token's row offset from `rows`; masked tokens (outside [0, T) or on an
-  // absent page) read row 0 of the sequence, whose values are finite
+  // absent page) read the finite row their entry names
   constexpr bool tok_list = TOK;
   const int64_t row_bytes = (int64_t)D * EB;
 
@@ -243,12 +244,13 @@ __device__ __forceinline__ void attend_bf16(const DecodeParams& p, int unit, con
   // Issue the loads of stage `st` of the table. Lanes of masked tokens load a
   // valid row of the same stage instead (their logits are -inf, so their p is
   // 0 and the finite V row adds nothing); an empty stage loads nothing.
-  const int64_t row0 = T > 0 ? max(row_offset(kv, b, g, 0), (int64_t)0) : 0;
+  // (a token list names its masked tokens' stand-in rows itself)
+  const int64_t row0 = !TOK && T > 0 ? max(row_offset(kv, b, g, 0), (int64_t)0) : 0;
   // byte offset of the row of list entry `e` (token list mode) and its validity
   auto token_row = [&](int e, bool& valid) {
     const int64_t off = rows[e];
     valid = off >= 0;
-    return valid ? off : row0;
+    return valid ? off : ~off;
   };
   // byte offset of token t of a stage that may straddle pages, and whether
   // its page is valid (a token on an absent page is masked like a token past
