@@ -762,26 +762,36 @@ __device__ __forceinline__ void topk_tokens(const SelectParams& p, int unit, con
   uint32_t total;
   const uint32_t at = wg_excl_scan((uint32_t)__popc(rest), sh.scan_tot[2], &total);
   const uint32_t cap = (uint32_t)p.out_cap;
-  int32_t* out = gids;
-  // position of kept slot u: at + the kept slots before it (no loop-carried
-  // state, so the 32 stores are independent predicated instructions)
-  auto store_all = [&](auto&& tok) {
+  // The kept candidates below the window take positions [0, n_rest): written
+  // to LDS (the transposition array, free since the scan's barrier) and copied
+  // out with coalesced stores when they fit there, else stored directly.
+  // Position of kept slot u: at + the kept slots before it (no loop-carried
+  // state, so the 32 writes are independent predicated instructions).
+  const uint32_t n_rest = min(total, cap);
+  auto store_all = [&](int32_t* out, auto&& tok) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const uint32_t pos = at + (uint32_t)__popc(rest & ((1u << u) - 1u));
       if (((rest >> u) & 1u) && pos < cap) out[pos] = tok(u);
     }
   };
-  if (S >= KPT)  // uniform
-    store_all([&](int u) {
-      const int r = r0 + u;
-      return (int)((r < S ? e0 : e1) * (uint32_t)S + (uint32_t)(r < S ? r : r - S));
-    });
-  else
-    store_all(token_of);
+  auto token_two = [&](int u) {  // S >= KPT: the slot's block is e0 or e1
+    const int r = r0 + u;
+    return (int)((r < S ? e0 : e1) * (uint32_t)S + (uint32_t)(r < S ? r : r - S));
+  };
+  if (n_rest <= (uint32_t)(kThreads * kRegKeys)) {  // uniform
+    int32_t* stage = reinterpret_cast<int32_t*>(sh.xpose);
+    if (S >= KPT) store_all(stage, token_two);  // uniform
+    else store_all(stage, token_of);
+    __syncthreads();
+    for (uint32_t i = tid; i < n_rest; i += kThreads) gids[i] = stage[i];
+  } else {
+    if (S >= KPT) store_all(gids, token_two);  // uniform
+    else store_all(gids, token_of);
+  }
   const int n_win = T - lo;
   for (int i = tid; i < n_win; i += kThreads)
-    if (total + (uint32_t)i < cap) out[total + i] = lo + i;
+    if (total + (uint32_t)i < cap) gids[total + i] = lo + i;
   if (tid == 0) *gcnt = (int)min(total + (uint32_t)n_win, cap);
 }
 
