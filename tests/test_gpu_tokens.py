@@ -34,6 +34,10 @@ CASES = {
                               top_k=200), 200, 300, 0),
     "regs-s16": (C[3].scaled(batch=2, hq=8, hkv=2, T=6001, seq_lens=(6001, 3100), S=16,
                              page_size=16, top_k=150), 150, 400, 40),
+    # more than 4096 kept tokens below the window: the register path stores
+    # them directly instead of through its LDS staging
+    "regs-many-kept": (C[3].scaled(batch=2, hq=8, hkv=2, T=8209, seq_lens=(8209, 5000),
+                                   top_k=240, window=64), 240, 5000, 64),
     "general-lds": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, S=8, page_size=8, top_k=600,
                                 window=64), 600, 700, 30),
     "general-ws": (C[3].scaled(batch=1, hq=8, hkv=2, T=8209, top_k=257), 257, 128, 64),
@@ -53,7 +57,8 @@ _P = {}
 
 
 # the top-k path each case must take
-PATHS = {"regs": "regs", "regs-wide": "regs", "regs-s16": "regs", "general-lds": "general",
+PATHS = {"regs": "regs", "regs-wide": "regs", "regs-s16": "regs", "regs-many-kept": "regs",
+         "general-lds": "general",
          "general-ws": "general", "f32-box": "regs", "d64-g8-pages": "regs", "mha-g1": "regs",
          "dense-scan": "general"}
 
