@@ -956,6 +956,10 @@ def shared_selection_timing(stream, reps):
                      "bytes_per_token": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
                      "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "mean_selected": mean_sel}
+    # HBM bytes per launch of the two kernels (layer 0's step, the other layers'
+    # decode), when a matching rocprofv3 summary exists
+    res["shared"]["traffic"] = {k: measured_traffic(k, w.name)
+                                for k in ("hs_decode_step", "hs_sparse_decode")}
     # the selection's drift: layer-0 selections over the workload's decode steps
     # (query q_t = 0.9 q_{t-1} + 0.44 n_t), |S_t minus S_t-1| per unit, untimed
     ws_s = hs.workspace(hs.hs_select_workspace_size(L0["kv"], L0["fine"], w.hq, w.top_k,
