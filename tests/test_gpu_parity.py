@@ -28,6 +28,11 @@ SMALL = {
     "c4s": C[4].scaled(batch=2, hq=2, hkv=2, T=16684, top_k=16, top_k_coarse=4,
                        seq_lens=(16684, 9000)),
     "c5s": C[5].scaled(batch=2, hq=8, hkv=2, T=4160, top_k=6, layers=3),
+    # 274 coarse blocks, more than one scoring chunk: the fused step refreshes
+    # both tables and selects the coarse level in three launches instead of
+    # its one-launch head
+    "c4s-many-coarse": C[4].scaled(batch=1, hq=2, hkv=2, T=70001, coarse_S=256, top_k=40,
+                                   top_k_coarse=8, needles=0),
     # two levels over box (min/max) fine summaries, fp32, GQA, d 64
     "c4s-box-f32-g4": C[4].scaled(batch=2, hq=8, hkv=2, d=64, T=9000, dtype="f32", kind="minmax",
                                   S=32, page_size=32, coarse_S=512, top_k=24, top_k_coarse=6,
