@@ -564,6 +564,7 @@ hs_status select_decode(const hs_select_params* prm, const hs_kv_cache* kv, cons
       h.fine_max_blocks = fine->max_blocks;
       h.fine_begin = refresh_begin;
       h.coarse_begin = cb;
+      h.status = reinterpret_cast<int32_t*>(ws + L.off_ctrl) + hs::kCtrlStatus;
       const hipError_t e = hs::launch_two_level_head(cp, h, s);
       if (e != hipSuccess) return from_hip(e);
     } else {

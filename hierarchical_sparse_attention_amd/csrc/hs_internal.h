@@ -240,19 +240,30 @@ struct SelectParams {
   int32_t out_blocks_max;    // blocks of this level per unit (bitmap bits)
   int32_t* counters;         // [units] workgroup arrivals; zero between calls
   int32_t refresh_begin;     // >= 0: rebuild blocks from here on before scoring (single level)
+  // With refresh_begin >= 0: when set, another workgroup of the launch
+  // rebuilds those blocks and then counts itself on the unit's word
+  // rebuilt_by + unit * kCounterStride; the scoring waits for that arrival
+  // (bounded by wait_ticks, an expiry recorded in *status) and takes it off
+  // again, so the word is zero between calls whatever the order.
+  int32_t* rebuilt_by = nullptr;
+  int32_t* status = nullptr;
+  long long wait_ticks = 0;
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 
-// Head of a two-level decode step, one launch: per unit (one workgroup), the
-// fine table's blocks from fine_begin are rebuilt (one wave each), then the
-// coarse table's blocks from coarse_begin (the whole workgroup each), then the
-// coarse selection runs on the refreshed table. `coarse` holds the coarse
-// level's selection parameters (its table is coarse.summ, of mean summaries,
-// and its candidates fit one scoring chunk).
+// Head of a two-level decode step, one launch of two workgroups per unit:
+// the first rebuilds the coarse table's blocks from coarse_begin (the whole
+// workgroup each), then the fine table's blocks from fine_begin (one wave
+// each); the second scores the unit's coarse rows meanwhile, rescores the
+// rebuilt ones once the first has stored them, and runs the coarse
+// selection. `coarse` holds the coarse level's selection parameters (its
+// table is coarse.summ, of mean summaries, and its candidates fit one
+// scoring chunk).
 struct HeadParams {
   void* fine;  // fine summary table
   int32_t fine_kind, fine_block, fine_max_blocks, fine_begin;
   int32_t coarse_begin;
+  int32_t* status;  // the step's status word (HS_STEP_WAIT_EXPIRED on an expired wait)
 };
 bool two_level_head_fits(const SelectParams& coarse, int32_t fine_block, int32_t coarse_kind);
 hipError_t launch_two_level_head(const SelectParams& coarse, const HeadParams& h, hipStream_t s);
@@ -314,6 +325,9 @@ struct StepParams {
   long long wait_ticks;      // bound of a wait, in wall-clock ticks (set by launch_step)
 };
 hipError_t launch_step(const StepParams& p, hipStream_t s);
+// Bound of a wait on another workgroup of a launch, in wall-clock ticks of
+// the current device (a quarter of a second).
+hipError_t wait_bound(long long* ticks);
 int step_chunks(int32_t n_slots_max);  // scoring tasks per unit
 // Whether the fused kernel's LDS (bitmap, keys, id list) fits for these sizes.
 bool step_fits(int32_t out_blocks_max, int32_t n_slots_max, int32_t list_cap);

@@ -22,10 +22,15 @@ __attribute__((amdgpu_waves_per_eu(KIND == kKindTokens ? 3 : 1))) void k_select(
 static_assert(sizeof(TopkShared) + HS_TOKEN_LDS_BYTES <= (160u << 10),
               "a token-level workgroup fits the LDS of a gfx950 workgroup");
 
-// Head of a two-level step (see HeadParams): refreshes, then the coarse
-// selection of the unit, whose candidates are one scoring chunk. The
-// rebuilt coarse rows are stored by this workgroup before its scoring loads
-// them (same compute unit and L2), so the scores see the new rows.
+// Head of a two-level step (see HeadParams), two workgroups per unit. The
+// builders (blocks [0, U)) rebuild the unit's growing coarse block(s), store
+// them, count themselves on the unit's rebuilt_by word, then rebuild the
+// growing fine block(s), which only the next launch reads. The selectors
+// (blocks [U, 2U)) score the unit's coarse rows from the table as it is,
+// wait for their builder's arrival, rescore the rebuilt rows with
+// device-coherent loads, and select; the coarse candidates are one scoring
+// chunk. Builders come first in the grid and never wait, so every
+// selector's wait ends.
 constexpr int kHeadUnroll = 16;  // K loads in flight per lane while rebuilding
 template <typename TE, int D, int FKIND, int G>
 __global__ __launch_bounds__(kThreads) void k_two_level_head(SelectParams p, HeadParams h,
@@ -38,10 +43,31 @@ __global__ __launch_bounds__(kThreads) void k_two_level_head(SelectParams p, Hea
   } sh;
   extern __shared__ uint32_t dyn[];
   const KvView& kv = p.kv;
+  const int U = kv.batch * kv.num_kv_heads;
+  if (blockIdx.x >= U) {  // selector
+    select_task<TE, D, HS_SUMMARY_MEAN, G>(p, blockIdx.x - U, 0, 1, sh.t, dyn,
+                                           reinterpret_cast<int32_t*>(dyn + list_off));
+    return;
+  }
   const int unit = blockIdx.x;
   const int b = unit / kv.num_kv_heads, g = unit % kv.num_kv_heads;
   const int wave = thread_id() / kWave;
   const int T = clamp_len(kv, b);
+  {  // coarse blocks: the whole workgroup each (uniform loop)
+    const int S = p.block_size;
+    const int nb = min((T + S - 1) / S, p.max_blocks);
+    for (int beta = h.coarse_begin; beta < nb; ++beta)
+      summarize_block_wg<TE, D, HS_SUMMARY_MEAN, kHeadUnroll, true>(  // read by the selector
+          kv, const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + beta, b, g, beta, S, T,
+          sh.seg);
+    __builtin_amdgcn_s_waitcnt(0);  // the rebuilt rows are stored, device-coherently
+    __syncthreads();
+    // the selector waits exactly when its chunk holds a rebuilt row (same
+    // unit_geom as the selector's)
+    if (thread_id() == 0 && h.coarse_begin < unit_geom(p, unit).n)
+      __hip_atomic_fetch_add(counter_of(p.rebuilt_by, unit), 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
   {  // fine blocks: one wave each
     const int S = h.fine_block;
     const int nb = min((T + S - 1) / S, h.fine_max_blocks);
@@ -49,24 +75,12 @@ __global__ __launch_bounds__(kThreads) void k_two_level_head(SelectParams p, Hea
       summarize_block<TE, D, FKIND, kHeadUnroll>(kv, h.fine, (int64_t)unit * h.fine_max_blocks + beta,
                                                  b, g, beta, S, T);
   }
-  {  // coarse blocks: the whole workgroup each (uniform loop)
-    const int S = p.block_size;
-    const int nb = min((T + S - 1) / S, p.max_blocks);
-    for (int beta = h.coarse_begin; beta < nb; ++beta)
-      summarize_block_wg<TE, D, HS_SUMMARY_MEAN, kHeadUnroll>(
-          kv, const_cast<void*>(p.summ), (int64_t)unit * p.max_blocks + beta, b, g, beta, S, T,
-          sh.seg);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // the rebuilt rows are stored
-  __syncthreads();
-  select_task<TE, D, HS_SUMMARY_MEAN, G>(p, unit, 0, 1, sh.t, dyn,
-                                         reinterpret_cast<int32_t*>(dyn + list_off));
 }
 
 template <typename TE, int D, int FKIND>
 hipError_t launch_head_g(const SelectParams& p, const HeadParams& h, size_t lds, int list_off,
                          hipStream_t s) {
-  const dim3 grid(p.kv.batch * p.kv.num_kv_heads);
+  const dim3 grid(2 * p.kv.batch * p.kv.num_kv_heads);  // builders, then selectors
   switch (p.G) {
     case 1: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 1>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
     case 2: hipLaunchKernelGGL((k_two_level_head<TE, D, FKIND, 2>), grid, dim3(kThreads), lds, s, p, h, list_off); break;
@@ -136,7 +150,15 @@ bool two_level_head_fits(const SelectParams& coarse, int32_t fine_block, int32_t
              (48u << 10);
 }
 
-hipError_t launch_two_level_head(const SelectParams& p, const HeadParams& h, hipStream_t s) {
+hipError_t launch_two_level_head(const SelectParams& coarse, const HeadParams& h, hipStream_t s) {
+  // the selectors rescore the rows their builders rebuild: the rebuilt-row
+  // arrivals take the second word of each unit's coarse counter line
+  SelectParams p = coarse;
+  p.refresh_begin = h.coarse_begin;
+  p.rebuilt_by = coarse.counters + 1;
+  p.status = h.status;
+  const hipError_t e = wait_bound(&p.wait_ticks);
+  if (e != hipSuccess) return e;
   const int list_off = (int)(select_lds_bytes(p.out_blocks_max, p.n_slots_max) / sizeof(uint32_t));
   const size_t lds = sizeof(uint32_t) * ((size_t)list_off + p.out_cap + kWave);
   const bool bf = p.kv.elem_bytes == 2;

@@ -1332,7 +1332,8 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
   constexpr int kTPW = kWave / (D / Vec16<TE>::EPL);  // tokens per K load instruction
   const int r0 = max(p.refresh_begin, c_wg), r1 = min(n_slots, c_wg + kRowsPerWG);
   const bool refresh = !kTok && p.refresh_begin >= 0 && p.gamma == nullptr && r0 < r1;  // uniform
-  const bool early = refresh && r1 - r0 <= kWaves && p.block_size <= kRefreshLoads * kTPW;
+  const bool early = refresh && p.rebuilt_by == nullptr && r1 - r0 <= kWaves &&
+                     p.block_size <= kRefreshLoads * kTPW;
   const int my_row = r0 + wave;
   uint4 rk[kRefreshLoads];
   uint32_t rk_ok = 0;
@@ -1385,12 +1386,28 @@ __device__ __forceinline__ void score_chunk(const SelectParams& p, int unit, int
         if (lane == 0) sh.stage[my_row - c_wg] = acc;
       }
     } else if (refresh) {
-      // more blocks than waves, or long blocks: rebuild, store, and score the
-      // stored rows (device-coherent loads)
-      for (int beta = r0 + wave; beta < r1; beta += kWaves)
-        summarize_block<TE, D, KIND, 4>(kv, const_cast<void*>(p.summ),
-                                     (int64_t)unit * p.max_blocks + beta, b, g, beta,
-                                     p.block_size, ug.T);
+      // more blocks than waves, or long blocks: rebuild and store (here, or by
+      // another workgroup, whose arrival is awaited), then score the stored
+      // rows (device-coherent loads)
+      if (p.rebuilt_by != nullptr) {
+        if (tid == 0) {
+          int32_t* w = counter_of(p.rebuilt_by, unit);
+          const long long t0 = wall_clock64();
+          for (int i = 0; published_i32(w) < 1; ++i) {
+            __builtin_amdgcn_s_sleep(2);
+            if ((i & 63) == 63 && wall_clock64() - t0 > p.wait_ticks) {
+              publish_i32(p.status, HS_STEP_WAIT_EXPIRED);
+              break;
+            }
+          }
+          __hip_atomic_fetch_add(w, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        for (int beta = r0 + wave; beta < r1; beta += kWaves)
+          summarize_block<TE, D, KIND, 4>(kv, const_cast<void*>(p.summ),
+                                       (int64_t)unit * p.max_blocks + beta, b, g, beta,
+                                       p.block_size, ug.T);
+      }
       __builtin_amdgcn_s_waitcnt(0);  // rebuilt rows are stored
       __syncthreads();                // (and the stale scores of those rows staged)
       for (int cb = r0 + wave * RPW; cb < r1; cb += kWaves * RPW) {  // wave-uniform

@@ -115,8 +115,10 @@ hipError_t resident_workgroups(const void* k, size_t lds, int* n) {
   return *n > 0 ? hipSuccess : hipErrorInvalidConfiguration;
 }
 
-// Bound of a wait on another workgroup: a quarter of a second of the
-// device's wall clock (a scoring task takes microseconds).
+}  // namespace
+
+// A quarter of a second of the device's wall clock (a scoring task takes
+// microseconds).
 hipError_t wait_bound(long long* ticks) {
   int dev = 0, khz = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -125,6 +127,8 @@ hipError_t wait_bound(long long* ticks) {
   *ticks = (long long)(khz > 0 ? khz : 100000) * 250;
   return hipSuccess;
 }
+
+namespace {
 
 template <typename TE, int D, int KIND, int G>
 hipError_t launch_one(StepParams p, size_t lds, int list_off, hipStream_t s) {

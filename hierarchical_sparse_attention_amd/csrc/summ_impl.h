@@ -128,7 +128,8 @@ __device__ __forceinline__ void summ_fold(float (&acc0)[Vec16<TE>::EPL],
   }
 }
 
-template <typename TE, int D, int KIND>
+// COHERENT: device-coherent stores (read by another workgroup of the launch)
+template <typename TE, int D, int KIND, bool COHERENT = false>
 __device__ __forceinline__ void summ_store(void* out, int64_t row,
                                            const float (&acc0)[Vec16<TE>::EPL],
                                            const float (&acc1)[Vec16<TE>::EPL], int n_tok);
@@ -163,8 +164,9 @@ constexpr int kSummWaves = 4;
 // (every thread calls it; blocks longer than a segment): in each round its
 // waves reduce the next kSummWaves segments side by side and wave 0 folds
 // them, in segment order, into the running values, so the row equals
-// summarize_block's. seg: LDS scratch of the workgroup.
-template <typename TE, int D, int KIND, int U>
+// summarize_block's. seg: LDS scratch of the workgroup. COHERENT: the row is
+// stored with device-coherent stores, for another workgroup of the launch.
+template <typename TE, int D, int KIND, int U, bool COHERENT = false>
 __device__ __forceinline__ void summarize_block_wg(
     const KvView& kv, void* out, int64_t row, int b, int g, int beta, int S, int T,
     float (*seg)[2][D / Vec16<TE>::EPL][Vec16<TE>::EPL]) {
@@ -211,7 +213,7 @@ __device__ __forceinline__ void summarize_block_wg(
     }
     __syncthreads();
   }
-  if (wave == 0) summ_store<TE, D, KIND>(out, row, acc0, acc1, t1 - t0);
+  if (wave == 0) summ_store<TE, D, KIND, COHERENT>(out, row, acc0, acc1, t1 - t0);
 }
 
 // The same summary as summarize_block for a block of at most NL * TPW
@@ -282,7 +284,7 @@ __device__ __forceinline__ void summ_reduce(const uint4 (&r)[NL], uint32_t ok,
 
 // Store of a reduced summary row (acc from summ_reduce; n valid tokens), as
 // summarize_block stores it.
-template <typename TE, int D, int KIND>
+template <typename TE, int D, int KIND, bool COHERENT>
 __device__ __forceinline__ void summ_store(void* out, int64_t row,
                                            const float (&acc0)[Vec16<TE>::EPL],
                                            const float (&acc1)[Vec16<TE>::EPL], int n_tok) {
@@ -294,10 +296,15 @@ __device__ __forceinline__ void summ_store(void* out, int64_t row,
   if (KIND == HS_SUMMARY_MEAN) {
     const float n = (float)n_tok;
     float* o = reinterpret_cast<float*>(out) + row * D + li * EPL;
+    if constexpr (COHERENT) {
 #pragma unroll
-    for (int k = 0; k < EPL; k += 4)
-      *reinterpret_cast<float4*>(o + k) =
-          make_float4(acc0[k] / n, acc0[k + 1] / n, acc0[k + 2] / n, acc0[k + 3] / n);
+      for (int k = 0; k < EPL; ++k) publish(o + k, acc0[k] / n);
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; k += 4)
+        *reinterpret_cast<float4*>(o + k) =
+            make_float4(acc0[k] / n, acc0[k + 1] / n, acc0[k + 2] / n, acc0[k + 3] / n);
+    }
   } else {
     uint4 lo, hi;
     if constexpr (EPL == 4) {
@@ -315,8 +322,19 @@ __device__ __forceinline__ void summ_store(void* out, int64_t row,
                       pack(acc1[6], acc1[7]));
     }
     uint8_t* o = reinterpret_cast<uint8_t*>(out) + row * 2 * D * (int64_t)sizeof(TE);
-    *reinterpret_cast<uint4*>(o + li * 16) = lo;
-    *reinterpret_cast<uint4*>(o + D * sizeof(TE) + li * 16) = hi;
+    if constexpr (COHERENT) {
+      int32_t* w0 = reinterpret_cast<int32_t*>(o + li * 16);
+      int32_t* w1 = reinterpret_cast<int32_t*>(o + D * sizeof(TE) + li * 16);
+      const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, c[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        publish_i32(w0 + k, (int32_t)a[k]);
+        publish_i32(w1 + k, (int32_t)c[k]);
+      }
+    } else {
+      *reinterpret_cast<uint4*>(o + li * 16) = lo;
+      *reinterpret_cast<uint4*>(o + D * sizeof(TE) + li * 16) = hi;
+    }
   }
 }
 

@@ -134,3 +134,53 @@ def test_overlapping_full_gpu_calls():
         expired += st != 0
     log("%d overlapping full-GPU calls on %d streams: %d equal to the separate calls, %d "
         "reported an expired wait" % (len(runs), len(streams), len(runs) - expired, expired))
+
+
+W2 = CONFIGS[4].scaled(batch=2, hq=2, hkv=2, T=16684, top_k=16, top_k_coarse=4, needles=0)
+
+
+def test_two_level_head_expired_wait_sets_status_word():
+    """The two-level step's head launch: a unit's coarse selector waits for
+    its builder's rebuilt-row arrival, counted on the second word of the
+    unit's coarse counter line. That word starts at -2^30 for unit 1, so the
+    wait cannot end and expires after the bound; every kernel exits, the
+    status word reads HS_STEP_WAIT_EXPIRED, the other units equal a normal
+    call's results, the bias stays (the builder's arrival and the selector's
+    take-off cancel), and after a zero-fill the workspace works normally."""
+    if "p2" not in _P:
+        log("setting up %s T=%d" % (W2.name, W2.T))
+        _P["p2"] = Problem.make(W2)
+    P = _P["p2"]
+    q = P.q()
+    summ = P.summaries()
+    last = W2.nb - 1
+    ids_r, cnt_r, out_r, ws_r = P.decode_step(q, summ, last)
+    torch.cuda.synchronize()
+    assert hs.hs_step_status(ws_r) == 0
+    n = hs.hs_select_decode_workspace_size(P.kvs[0], summ["fine"], W2.hq, W2.top_k, W2.window,
+                                           ids_r.shape[-1], summ["coarse"], W2.top_k_coarse)
+    ws = hs.workspace(n, "cuda")
+    unit, units = 1, W2.batch * W2.hkv
+    at = (hs.STEP_SELECT_BYTE + 256 * units + 256 * unit + 4) // 4  # coarse line, word 1
+    ws.view(torch.int32)[at] = -(1 << 30)
+    torch.cuda.synchronize()
+    log("calling the two-level hs_decode_step with unit %d's rebuilt-row word at -2^30" % unit)
+    ids, cnt, out, _ = P.decode_step(q, summ, last, ws=ws)
+    torch.cuda.synchronize()
+    assert hs.hs_step_status(ws) == hs.HS_STEP_WAIT_EXPIRED
+    b, g = divmod(unit, W2.hkv)
+    for bb in range(W2.batch):
+        for gg in range(W2.hkv):
+            if (bb, gg) == (b, g):
+                continue
+            c = int(cnt_r[bb, gg])
+            assert int(cnt[bb, gg]) == c and torch.equal(ids[bb, gg, :c], ids_r[bb, gg, :c])
+            hq = slice(gg * W2.G, (gg + 1) * W2.G)
+            assert torch.equal(out[bb, hq], out_r[bb, hq]), (bb, gg)
+    assert int(ws.view(torch.int32)[at]) == -(1 << 30)
+    ws.zero_()
+    ids, cnt, out, _ = P.decode_step(q, summ, last, ws=ws)
+    torch.cuda.synchronize()
+    assert hs.hs_step_status(ws) == 0
+    assert torch.equal(ids, ids_r) and torch.equal(cnt, cnt_r) and torch.equal(out, out_r)
+    log("head's expired wait reported; workspace reusable after a zero-fill")
