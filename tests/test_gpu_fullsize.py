@@ -162,3 +162,50 @@ def test_maximum_blocks_per_unit():
     log("max blocks: %d selected of %d blocks" % (cnt[0, 0], w.nb))
     del P
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_token_stage():
+    """The token-level second stage at the 128K workload's full size, as the
+    benchmark's token figure runs it ("SparDA" article, section 2.3): on the
+    block selection of hs_decode_step, hs_select_tokens keeps the top 1024
+    tokens of the selected blocks plus the 512 window tokens, and
+    hs_sparse_decode with block size 1 attends over them. Sampled units:
+    token ids against the oracle under the near-tie rule, outputs against the
+    oracle's attention over the kept tokens."""
+    from gpu_helpers import check_tokens
+    w = CONFIGS[3]
+    k_tok, window = 1024, 512
+    log("token stage at config 3 (%s): generating and uploading inputs" % w.name)
+    P = Problem.make(w)
+    kv = P.kvs[0]
+    q = P.q()
+    summ = P.summaries()
+    ids_t, cnt_t, _, _ = P.decode_step(q, summ, (w.T - 1) // w.S)
+    ms = ids_t.shape[-1]
+    max_tok = min(ms * w.S, k_tok) + min(window, w.T)
+    tok = torch.full((w.batch, w.hkv, max_tok), -7, dtype=torch.int32, device="cuda")
+    tcnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+    ws = hs.workspace(hs.hs_select_tokens_workspace_size(kv, w.hq, w.S, ms, k_tok, window,
+                                                         max_tok), "cuda")
+    hs.hs_select_tokens(kv, q, w.S, ids_t, cnt_t, k_tok, window, tok, tcnt, ws)
+    out = P.decode(q, tok, tcnt, block_size=1)
+    torch.cuda.synchronize()
+    ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+    t_ids, t_cnt = tok.cpu().numpy(), tcnt.cpu().numpy()
+    o = out.cpu().double().numpy()
+    # the top 1024 and the window overlap where window tokens score high
+    assert np.all(t_cnt >= window) and np.all(t_cnt <= k_tok + window), t_cnt.reshape(-1).tolist()
+    ties = 0
+    for b, g in sample_units(w, 4):
+        T = w.T
+        qo, K, V = unit_inputs(w, 0, b, g)
+        blocks = ids[b, g, :cnt[b, g]]
+        ref, scores, kth = oracle.select_tokens_unit(qo, K, T, blocks, w.S, k_tok, window)
+        gi = t_ids[b, g, :t_cnt[b, g]]
+        what = "token stage config 3 unit (%d,%d)" % (b, g)
+        ties += check_tokens(gi, ref, scores, kth, qo, K, T, window, what)
+        check_rows(w, o[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, 1), what)
+    log("token stage config 3: %d tolerated near-tie differences" % ties)
+    del P
+    torch.cuda.empty_cache()
