@@ -209,3 +209,53 @@ def test_full_size_token_stage():
     log("token stage config 3: %d tolerated near-tie differences" % ties)
     del P
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_ratio_and_reserve():
+    """hs_decode_step at the 128K workload's full size with the benchmark's
+    ratio-and-reserve settings ("SparDA" article, sections 3.2 and 3.4): k from
+    the length-scheduled ratio (5 % of 4096 blocks = 204) instead of a fixed k,
+    and a seeded reserve set of 1 % of the blocks (40 per unit) forced in.
+    Sampled units against the oracle: ids under the near-tie rule with every
+    reserve block kept, outputs within the per-row bound."""
+    w = CONFIGS[3]
+    ratio, nb = 0.05, w.nb
+    k = max(1, int(nb * float(np.float32(ratio))))
+    r = max(1, int(nb * 0.01))
+    rng = np.random.default_rng(w.seed + 7)  # the benchmark's draw
+    forced = np.stack([rng.choice(nb, size=r, replace=False) for _ in range(w.units)])
+    forced = forced.astype(np.int32).reshape(w.batch, w.hkv, r)
+    forced_t = torch.from_numpy(forced).cuda()
+    cap = min(nb, k + -(-w.window // w.S) + 1 + r)
+    log("ratio and reserve at config 3: k %d, %d reserve blocks per unit, capacity %d" % (k, r, cap))
+    P = Problem.make(w)
+    kv = P.kvs[0]
+    q = P.q()
+    summ = P.summaries()
+    ids_t = torch.full((w.batch, w.hkv, cap), -7, dtype=torch.int32, device="cuda")
+    cnt_t = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+    out_t = torch.full((w.batch, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    n = hs.hs_select_decode_workspace_size(kv, summ["fine"], w.hq, w.top_k, w.window, cap,
+                                           top_k_ratio=ratio, forced=forced_t)
+    hs.hs_decode_step(kv, q, summ["fine"], w.top_k, w.window, (w.T - 1) // w.S, ids_t, cnt_t,
+                      out_t, hs.workspace(n, "cuda"), top_k_ratio=ratio, forced=forced_t)
+    torch.cuda.synchronize()
+    ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+    o = out_t.cpu().double().numpy()
+    ties = 0
+    for b, g in sample_units(w, 4):
+        T = w.T
+        qo, K, V = unit_inputs(w, 0, b, g)
+        f = forced[b, g]
+        sel = oracle.select_unit(qo, K, T, w.kind, w.S, w.top_k, w.window, top_k_ratio=ratio,
+                                 forced=f)
+        gi = ids[b, g, :cnt[b, g]]
+        what = "ratio and reserve config 3 unit (%d,%d)" % (b, g)
+        assert set(f.tolist()) <= set(gi.tolist()), what
+        ties += check_ids(w, gi, sel, magnitudes(w, qo, K, T), T, what=what)
+        check_rows(w, o[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, w.S), what)
+    log("ratio and reserve config 3: %d tolerated near-tie differences, mean count %.1f" % (
+        ties, cnt.mean()))
+    del P
+    torch.cuda.empty_cache()
