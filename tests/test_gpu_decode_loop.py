@@ -119,3 +119,72 @@ def test_decode_loop_with_appends_matches_oracle(name):
                                                           torch.bfloat16 else torch.int32)), \
                 (name, key, b)
     log("%s: %d steps, %d tolerated near-tie differences" % (name, steps, ties))
+
+
+@pytest.mark.timeout(900)
+def test_decode_loop_full_size_sampled():
+    """The 128K workload at full size, as the benchmark's decode-loop figure
+    runs it: 8 steps of hs_append_kv + hs_decode_step from lengths just below
+    the cache's 131072 tokens (sequence 1 crosses a 32-token block boundary),
+    rows past each starting length poisoned with NaN first. The appended rows
+    are the generator's, copied out of the pools before the poisoning. Four
+    sampled units are checked against the oracle at every step; at the end the
+    refreshed tables equal a full rebuild."""
+    base = C[3]
+    start = (base.T - 8, base.T - 35, base.T - 3, base.T - 20)
+    w = base.scaled(seq_lens=start)
+    steps = 8
+    log("config 3 decode loop at full size: %d steps from lengths %s" % (steps, start))
+    P = Problem.make(w)
+    kv = P.kvs[0]
+    pt = w.page_table()
+    new_rows = {}
+    for b in range(w.batch):
+        t = np.arange(start[b], w.T)
+        pages = torch.from_numpy(pt[b][t // w.page_size].astype(np.int64)).cuda()
+        slots = torch.from_numpy(t % w.page_size).cuda()
+        new_rows[b] = (kv.k_pool[pages, :, slots].clone(), kv.v_pool[pages, :, slots].clone())
+    poison_tail(w, P)
+    summ = P.summaries()
+    units = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    rows = {u: unit_inputs(w, 0, u[0], u[1]) for u in units}
+    lens = list(start)
+    ws = None
+    ties = 0
+    for s in range(steps):
+        k_new = torch.zeros((w.batch, w.hkv, w.d), dtype=kv.k_pool.dtype, device="cuda")
+        v_new = torch.zeros_like(k_new)
+        for b in range(w.batch):
+            if lens[b] < w.T:
+                k_new[b] = new_rows[b][0][lens[b] - start[b]]
+                v_new[b] = new_rows[b][1][lens[b] - start[b]]
+        hs.hs_append_kv(kv, k_new, v_new)
+        lens = [min(t + 1, w.T) for t in lens]
+        refresh = min((t - 1) // w.S for t in lens)
+        ids_t, cnt_t, out_t, ws = P.decode_step(P.q(0, s), summ, refresh, ws=ws)
+        torch.cuda.synchronize()
+        assert kv.seq_lens.cpu().tolist() == lens, (s, kv.seq_lens.cpu().tolist(), lens)
+        ids, cnt = ids_t.cpu().numpy(), cnt_t.cpu().numpy()
+        out = out_t.cpu().double().numpy()
+        for (b, g), (_, K, V) in rows.items():
+            T = lens[b]
+            qo = unit_inputs(w, 0, b, g, s)[0]
+            sel = oracle_select(w, qo, K, T)
+            gi = ids[b, g, :cnt[b, g]]
+            what = "config 3 loop step %d unit (%d,%d) T=%d" % (s, b, g, T)
+            ties += check_ids(w, gi, sel, magnitudes(w, qo, K, T), T, what=what)
+            check_rows(w, out[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, w.S),
+                       what)
+    for key, tab in summ.items():
+        fresh = hs.Summaries(torch.empty_like(tab.data), tab.kind, tab.block_size)
+        hs.hs_build_summaries(kv, fresh)
+        torch.cuda.synchronize()
+        for b in range(w.batch):
+            nb = -(-lens[b] // tab.block_size)
+            view = torch.int16 if tab.data.dtype == torch.bfloat16 else torch.int32
+            assert torch.equal(tab.data[b, :, :nb].view(view), fresh.data[b, :, :nb].view(view)), \
+                (key, b)
+    log("config 3 decode loop: %d steps, lengths %s, %d tolerated near-tie differences" % (
+        steps, lens, ties))
+    del P
+    torch.cuda.empty_cache()
