@@ -145,3 +145,52 @@ def test_token_list_attention_skips_invalid_ids(name):
         qo, K, V = unit_inputs(w, 0, b, g)
         ref = oracle.attend_unit(qo, K, V, T, good, 1)
         check_rows(w, o[b, g * w.G:(g + 1) * w.G], ref, "%s invalid ids (%d,%d)" % (name, b, g))
+
+
+@pytest.mark.parametrize("name", ["regs", "general-ws"])
+def test_token_stage_empty_lists_and_sequences(name):
+    """Degenerate inputs of the token stage: a unit with no selected blocks
+    keeps only its window's tokens (the window is attended whether scored or
+    not), a sequence of length 0 keeps nothing and attends to nothing (output
+    row 0), and every other unit is unaffected; the token ids match the
+    oracle and the attention over them matches the oracle's."""
+    w0, kb, kt, wt = CASES[name]
+    lens = (w0.T, 0) if w0.batch == 2 else (w0.T,)
+    w = w0.scaled(seq_lens=lens) if w0.batch == 2 else w0
+    P = Problem.make(w)
+    kv = P.kvs[0]
+    q = P.q()
+    summ = P.summaries()
+    ids, cnt = P.select(q, summ, top_k=kb)
+    ms = ids.shape[-1]
+    cnt[0, 0] = 0  # unit (0, 0): an empty block list
+    max_tok = min(ms * w.S, kt) + min(wt, w.T)
+    tok = torch.full((w.batch, w.hkv, max_tok), -7, dtype=torch.int32, device="cuda")
+    tcnt = torch.full((w.batch, w.hkv), -7, dtype=torch.int32, device="cuda")
+    ws = hs.workspace(hs.hs_select_tokens_workspace_size(kv, w.hq, w.S, ms, kt, wt, max_tok),
+                      "cuda")
+    hs.hs_select_tokens(kv, q, w.S, ids, cnt, kt, wt, tok, tcnt, ws)
+    out = P.decode(q, tok, tcnt, block_size=1)
+    torch.cuda.synchronize()
+    b_ids, b_cnt = ids.cpu().numpy(), cnt.cpu().numpy()
+    t_ids, t_cnt = tok.cpu().numpy(), tcnt.cpu().numpy()
+    o = out.cpu().double().numpy()
+    seq = w.seq_lens_array()
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            T = int(seq[b])
+            qo, K, V = unit_inputs(w, 0, b, g)
+            blocks = b_ids[b, g, :b_cnt[b, g]]
+            ref, scores, kth = oracle.select_tokens_unit(qo, K, T, blocks, w.S, kt, wt)
+            gi = t_ids[b, g, :t_cnt[b, g]]
+            what = "%s degenerate unit (%d,%d) T=%d, %d blocks" % (name, b, g, T, len(blocks))
+            if (b, g) == (0, 0):
+                assert np.array_equal(gi, np.arange(max(0, T - wt), T, dtype=np.int32)), what
+            if T == 0:
+                assert len(gi) == 0, what
+                assert np.all(o[b, g * w.G:(g + 1) * w.G] == 0.0), what
+                continue
+            check_tokens(gi, ref, scores, kth, qo, K, T, wt, what)
+            check_rows(w, o[b, g * w.G:(g + 1) * w.G], oracle.attend_unit(qo, K, V, T, gi, 1),
+                       what)
+    log("%s degenerate lists: token counts %s" % (name, t_cnt.reshape(-1).tolist()))
