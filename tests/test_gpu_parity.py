@@ -28,6 +28,10 @@ SMALL = {
     "c4s": C[4].scaled(batch=2, hq=2, hkv=2, T=16684, top_k=16, top_k_coarse=4,
                        seq_lens=(16684, 9000)),
     "c5s": C[5].scaled(batch=2, hq=8, hkv=2, T=4160, top_k=6, layers=3),
+    # top_k_coarse above the 9 coarse blocks: every coarse block is kept and
+    # the fine level ranks every fine block, as a single level would
+    "c4s-all-coarse": C[4].scaled(batch=1, hq=2, hkv=2, T=9000, top_k=20, top_k_coarse=12,
+                                  needles=0),
     # 274 coarse blocks, more than one scoring chunk: the fused step refreshes
     # both tables and selects the coarse level in three launches instead of
     # its one-launch head
